@@ -1,0 +1,69 @@
+"""CPU oracle for the routed MoE expert step (test infrastructure only).
+
+This package is the plain, slow, obviously correct CPU statement of what the
+hot path computes. It exists to check the HIP library, nothing else: only the
+test suite, the smoke check and the benchmark's CPU-baseline leg import it.
+The HIP library and its Python binding never import, link or execute anything
+from here, and this package imports nothing from them.
+
+Sources (the three web pages the method is taken from):
+
+* "Grouped expert GEMM: schedule irregular rows without changing the experts"
+  (study.greatitself.com, expert-parallel training notes) -- FLOP convention,
+  edge cases, the roofline lab.
+* "Section 09: Grouped GEMM" of the OLMo-core MoE report (taotianhua.com) --
+  Eq 13 (SwiGLU expert), Eq 14 (padding fraction), Figs 35-37 (the four-expert
+  toy), Eq 16 (capacity), Eq 17 (column partition), Eq 18 (entropy deficit).
+* "Grouped GEMM" engineering notes of the halo training toolkit (github) --
+  drop of out-of-range expert ids before the sort, contiguous per-expert
+  blocks, int32 cumulative offsets, the inverse map used by the atomic-free
+  unpermute, the gate-then-up weight layout.
+
+Numerics: every contraction is evaluated in float64 on bf16-valued operands
+(the products of two bf16 values are exact in float64 and sums of a few
+thousand of them keep ~40 bits of headroom), and results are rounded to bf16
+with round-to-nearest-even exactly where the method stores a bf16 tensor.
+``precision="f32"`` instead runs the per-expert loop in float32, the form in
+which the method states its accumulation; the test suite pins the two against
+each other within the float32 error bound.
+"""
+
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
+from .moe import (
+    MoeOracleResult,
+    capacity_ceil,
+    capacity_eq16,
+    entropy_deficit,
+    exclusive_offsets,
+    expert_forward,
+    moe_expert_forward,
+    padding_fraction,
+    permute_rows,
+    route_histogram,
+    stable_route_order,
+    tile_count,
+    token_forward,
+    unpermute,
+    useful_flops,
+)
+
+__all__ = [
+    "MoeOracleResult",
+    "bf16_bits_to_f64",
+    "capacity_ceil",
+    "capacity_eq16",
+    "entropy_deficit",
+    "exclusive_offsets",
+    "expert_forward",
+    "f64_to_bf16_bits",
+    "moe_expert_forward",
+    "padding_fraction",
+    "permute_rows",
+    "round_to_bf16",
+    "route_histogram",
+    "stable_route_order",
+    "tile_count",
+    "token_forward",
+    "unpermute",
+    "useful_flops",
+]

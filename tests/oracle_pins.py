@@ -1,0 +1,293 @@
+"""Pins that tie the oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+something the pages print, a closed form, a textbook/library routine applied
+to a special case, brute force on a tiny input, or an exact invariance. The
+functions take the oracle package as an argument so the mutation tests can run
+them against an oracle with a planted mistake and see them fail.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from workloads import make_random, make_workload, to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "toy_figs35_37.json")
+
+
+def golden() -> dict:
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _bits_to_f64(b):
+    return torch.from_numpy(np.asarray(b, dtype=np.uint16).view(np.int16).copy()).view(torch.bfloat16).double()
+
+
+def _torch_bf16_bits(t64: torch.Tensor) -> np.ndarray:
+    """Library rounding for the independent references: float64 -> float32 -> bfloat16 (torch)."""
+    return t64.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _ulps(a, b):
+    a = np.asarray(a, dtype=np.uint16).astype(np.int64)
+    b = np.asarray(b, dtype=np.uint16).astype(np.int64)
+    oa = np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF)
+    ob = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(oa - ob)
+
+
+def _assert_close_bits(got, ref, what, min_exact=0.99, max_ulp=1):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    u = _ulps(got, ref)
+    exact = float(np.mean(u == 0)) if u.size else 1.0
+    assert exact >= min_exact, f"{what}: only {exact:.4f} of elements bit-identical"
+    assert (u.max() if u.size else 0) <= max_ulp, f"{what}: max ulp difference {u.max()}"
+
+
+# ---------------------------------------------------------------- printed toy
+
+
+def pin_toy_golden(orc) -> None:
+    """Figs 35-37: rows (1,4,3,2) -> offsets [1,5,8,10], C=4, rho=0.375, 16 rows, 12 tiles."""
+    g = golden()["toy"]
+    wl = make_workload("toy")
+    counts = orc.route_histogram(wl.expert_ids, wl.E)
+    assert counts.tolist() == g["rows_per_expert"]
+    offsets = orc.exclusive_offsets(counts)
+    assert offsets[0] == 0 and offsets[1:].tolist() == g["cumulative_offsets_inclusive"]
+    M = int(offsets[-1])
+    assert M == g["routed_rows_M"]
+    assert M / wl.E == g["mean_load"]
+    C = orc.capacity_ceil(g["capacity_factor"], M, wl.E)
+    assert C == g["capacity_C"]
+    assert wl.E * C == g["rows_multiplied_padded"]
+    assert wl.E * C - M == g["padding_rows"]
+    assert orc.padding_fraction(counts, C) == g["padding_fraction"]
+    slices = [[int(offsets[e]), int(offsets[e + 1])] for e in range(wl.E)]
+    assert slices == g["problem_row_slices"]
+    assert orc.tile_count(counts, g["tile_rows"], g["tile_col_blocks"]) == g["tiles"]
+    perm, inv = orc.stable_route_order(wl.expert_ids, wl.E, offsets)
+    assert sorted(inv.tolist()) == list(range(*g["computed_rows"]))
+    # every sorted row carries its own expert's id
+    flat = wl.expert_ids.reshape(-1)
+    for e, (lo, hi) in enumerate(slices):
+        assert all(flat[perm[p]] == e for p in range(lo, hi))
+
+
+def pin_printed_arithmetic(orc) -> None:
+    """Fig 38 / Fig 39 / Sec 9.6 numbers recomputed from the FLOP convention and Eq 14."""
+    gd = golden()
+    f = gd["fig38"]
+    # One projection of a gated expert is a third of 6*M*d*h (two FLOPs per multiply-add).
+    proj = orc.useful_flops(f["M"], f["d"], f["h"]) // 3
+    assert proj == 2 * f["M"] * f["d"] * f["h"]
+    lo_t, hi_t = f["grouped_ms"] - 5e-4, f["grouped_ms"] + 5e-4  # printed to 3 decimals
+    assert proj / (hi_t * 1e-3) / 1e12 <= f["grouped_tflops"] <= proj / (lo_t * 1e-3) / 1e12
+    lo_b, hi_b = f["bmm_ms"] - 5e-4, f["bmm_ms"] + 5e-4
+    assert proj / (hi_b * 1e-3) / 1e12 <= f["bmm_useful_tflops"] + 0.5
+    assert f["bmm_useful_tflops"] - 0.5 <= proj / (lo_b * 1e-3) / 1e12
+    C = orc.capacity_ceil(1.25, f["M"], f["experts"])
+    assert C == f["bmm_capacity_C"] and f["experts"] * C == f["bmm_rows"]
+    padded = 2 * f["bmm_rows"] * f["d"] * f["h"]
+    assert padded / (hi_b * 1e-3) / 1e12 <= f["bmm_padded_tflops"] + 0.5
+    assert f["bmm_padded_tflops"] - 0.5 <= padded / (lo_b * 1e-3) / 1e12
+    counts = np.full(f["experts"], f["rows_per_expert"])
+    assert orc.padding_fraction(counts, C) == gd["sec96_capacity"]["padding_fraction_balanced"]
+    f39 = gd["fig39"]
+    assert round(2 * f39["T"] * f39["K"] * f39["N"] / 1e12, 2) == f39["tflop_rounded"]
+    # Eq 16 on the toy with one EP rank: 8 * ceil(floor(1.25 * 2.5) / 8) = 8 (derived)
+    assert orc.capacity_eq16(1.25, 2.5, 1) == 8
+    assert orc.capacity_eq16(1.25, 512, 1) == 640
+    e18 = gd["eq18"]
+    assert orc.entropy_deficit(np.full(16, 7)) == e18["uniform"]
+    assert abs(orc.entropy_deficit(np.eye(16, dtype=int)[3] * 99) - e18["single_expert"]) < 1e-15
+
+
+# ------------------------------------------------------------ library routines
+
+
+def pin_histogram_and_order(orc, seeds=(0, 1, 2)) -> None:
+    """counts = numpy.bincount, offsets = [0, cumsum], perm = stable argsort (library routines)."""
+    for seed in seeds:
+        wl = make_random(T=97, k=3, E=7, d=8, h=8, seed=seed, drop_frac=0.2)
+        flat = wl.expert_ids.reshape(-1).astype(np.int64)
+        valid = (flat >= 0) & (flat < wl.E)
+        counts = orc.route_histogram(wl.expert_ids, wl.E)
+        np.testing.assert_array_equal(counts, np.bincount(flat[valid], minlength=wl.E))
+        offsets = orc.exclusive_offsets(counts)
+        np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+        perm, inv = orc.stable_route_order(wl.expert_ids, wl.E, offsets)
+        slots = np.flatnonzero(valid)
+        order = slots[np.argsort(flat[valid], kind="stable")]
+        M = int(valid.sum())
+        np.testing.assert_array_equal(perm[:M], order)
+        assert np.all(inv[~valid] == -1)
+        assert np.all(perm[inv[valid]] == slots)
+        assert sorted(inv[valid].tolist()) == list(range(M))
+
+
+def pin_permute_unpermute_identity(orc) -> None:
+    """Unpermute(permute(X)) = X: bit-exact at k=1, w=1; and at k>1 when the weights sum to 1."""
+    wl = make_random(T=64, k=1, E=5, d=24, h=8, seed=11, drop_frac=0.15)
+    wl.routing_w[:] = 1.0
+    r = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, with_gemm=False)
+    y = orc.unpermute(r.x_perm, r.inv_map, wl.routing_w, wl.T, wl.k)
+    kept = (r.inv_map[:, 0] >= 0)
+    np.testing.assert_array_equal(y[kept], wl.x[kept])
+    assert np.all(y[~kept] == 0)
+    wl = make_random(T=64, k=4, E=5, d=24, h=8, seed=12, drop_frac=0.0)  # softmax weights, sum 1
+    r = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, with_gemm=False)
+    y = orc.unpermute(r.x_perm, r.inv_map, wl.routing_w, wl.T, wl.k)
+    np.testing.assert_array_equal(y, wl.x)
+
+
+def _dense_swiglu_torch(x_bits, wg_bits, wu_bits, wd_bits):
+    """A dense SwiGLU MLP through torch library ops in float64, bf16-rounded (torch) at the
+    points the method stores bf16: U, H, Y."""
+    x = _bits_to_f64(x_bits)
+    g = _bits_to_f64(_torch_bf16_bits(F.linear(x, _bits_to_f64(wg_bits))))
+    u = _bits_to_f64(_torch_bf16_bits(F.linear(x, _bits_to_f64(wu_bits))))
+    hid = _bits_to_f64(_torch_bf16_bits(F.silu(g) * u))
+    return _torch_bf16_bits(hid @ _bits_to_f64(wd_bits))
+
+
+def pin_single_expert_is_dense_mlp(orc) -> None:
+    """E = 1 with k = 1 and w = 1: the expert step is a dense SwiGLU MLP (torch F.linear / F.silu)."""
+    rng = np.random.default_rng(5)
+    T, d, h = 48, 40, 24  # d != h and d != 2h so a transposed operand cannot pass
+    x = to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    w_ug = to_bf16_bits(0.2 * rng.standard_normal((1, 2 * h, d), dtype=np.float32))
+    w_dn = to_bf16_bits(0.2 * rng.standard_normal((1, h, d), dtype=np.float32))
+    ids = np.zeros((T, 1), dtype=np.int32)
+    w = np.ones((T, 1), dtype=np.float32)
+    r = orc.moe_expert_forward(x, ids, w, w_ug, w_dn)
+    ref = _dense_swiglu_torch(x, w_ug[0, :h], w_ug[0, h:], w_dn[0])
+    _assert_close_bits(r.y, ref, "E=1 dense SwiGLU", min_exact=0.99, max_ulp=1)
+
+
+def pin_column_partition(orc) -> None:
+    """Eq 17: with every token on every expert and w = 1, the experts are column blocks of one
+    dense SwiGLU MLP of hidden width E*h (gate blocks, up blocks and down blocks concatenated)."""
+    rng = np.random.default_rng(9)
+    T, E, d, h = 20, 3, 32, 16
+    x = to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    w_ug = to_bf16_bits(0.2 * rng.standard_normal((E, 2 * h, d), dtype=np.float32))
+    w_dn = to_bf16_bits(0.2 * rng.standard_normal((E, h, d), dtype=np.float32))
+    ids = np.tile(np.arange(E, dtype=np.int32), (T, 1))
+    w = np.ones((T, E), dtype=np.float32)
+    r = orc.moe_expert_forward(x, ids, w, w_ug, w_dn)
+    wg = np.concatenate([w_ug[e, :h] for e in range(E)], axis=0)  # [E*h, d]
+    wu = np.concatenate([w_ug[e, h:] for e in range(E)], axis=0)
+    wd = np.concatenate([w_dn[e] for e in range(E)], axis=0)  # [E*h, d]
+    xt = _bits_to_f64(x)
+    g = _bits_to_f64(_torch_bf16_bits(F.linear(xt, _bits_to_f64(wg))))
+    u = _bits_to_f64(_torch_bf16_bits(F.linear(xt, _bits_to_f64(wu))))
+    hid = _bits_to_f64(_torch_bf16_bits(F.silu(g) * u))
+    dense = (hid @ _bits_to_f64(wd)).numpy()  # unrounded dense result
+    got = _bits_to_f64(r.y).numpy()
+    # the grouped form rounds each expert's Y_e to bf16 before the sum: E half-ulps of |Y_e|
+    tol = (E + 1) * 2.0**-8 * np.abs(dense).max()
+    assert np.max(np.abs(got - dense)) <= tol, f"Eq 17 partition off by {np.max(np.abs(got - dense))}"
+    assert np.linalg.norm(got - dense) <= 2.0**-7 * np.linalg.norm(dense)
+
+
+def pin_brute_force(orc) -> None:
+    """Pure-Python loops over every index of Eq 13 and the weighted scatter-back on a tiny case."""
+    T, k, E, d, h = 7, 2, 3, 8, 8  # d == h: a transposed weight would still type-check here
+    wl = make_random(T=T, k=k, E=E, d=d, h=h, seed=21, drop_frac=0.2, w_sigma=0.3)
+    r = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
+    xv = _bits_to_f64(wl.x).tolist()
+    wug = _bits_to_f64(wl.w_ug).tolist()
+    wdn = _bits_to_f64(wl.w_down).tolist()
+
+    def rb(v):  # torch's float32 -> bfloat16 rounding, one scalar
+        return float(torch.tensor(v, dtype=torch.float64).float().to(torch.bfloat16).double())
+
+    ref = np.zeros((T, d), dtype=np.uint16)
+    for t in range(T):
+        acc = [0.0] * d
+        for j in range(k):
+            e = int(wl.expert_ids[t, j])
+            if not 0 <= e < E:
+                continue
+            U = [rb(sum(xv[t][c] * wug[e][n][c] for c in range(d))) for n in range(2 * h)]
+            H = [rb(U[n] / (1.0 + math.exp(-U[n])) * U[h + n]) for n in range(h)]
+            Y = [rb(sum(H[n] * wdn[e][n][c] for n in range(h))) for c in range(d)]
+            wj = float(wl.routing_w[t, j])
+            acc = [acc[c] + wj * Y[c] for c in range(d)]
+        ref[t] = _torch_bf16_bits(torch.tensor(acc, dtype=torch.float64))
+    _assert_close_bits(r.y, ref, "brute force", min_exact=0.97, max_ulp=1)
+
+
+def pin_invariances(orc) -> None:
+    """Exact invariances: w -> 2w doubles y; relabeling experts (with their weights), adding an
+    empty expert, or shuffling tokens (with ids and weights) leaves every token's y unchanged."""
+    wl = make_random(T=40, k=3, E=6, d=32, h=16, seed=31, drop_frac=0.1, w_sigma=0.2)
+    base = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
+    ref = _bits_to_f64(base.y).numpy()
+    r2 = orc.moe_expert_forward(wl.x, wl.expert_ids, 2 * wl.routing_w, wl.w_ug, wl.w_down)
+    np.testing.assert_array_equal(_bits_to_f64(r2.y).numpy(), 2 * ref)
+    rng = np.random.default_rng(3)
+    relabel = rng.permutation(wl.E)  # old id -> new id
+    ids = wl.expert_ids.copy()
+    valid = (ids >= 0) & (ids < wl.E)
+    ids[valid] = relabel[ids[valid]]
+    inv_label = np.argsort(relabel)
+    r3 = orc.moe_expert_forward(wl.x, ids, wl.routing_w, wl.w_ug[inv_label], wl.w_down[inv_label])
+    np.testing.assert_array_equal(r3.y, base.y)
+    extra_ug = np.concatenate([wl.w_ug, to_bf16_bits(rng.standard_normal((1,) + wl.w_ug.shape[1:],
+                                                                          dtype=np.float32))])
+    extra_dn = np.concatenate([wl.w_down, to_bf16_bits(rng.standard_normal((1,) + wl.w_down.shape[1:],
+                                                                           dtype=np.float32))])
+    ids4 = wl.expert_ids.copy()
+    ids4[ids4 == wl.E] = -1  # with E+1 experts, an id equal to the old E would become valid
+    r4 = orc.moe_expert_forward(wl.x, ids4, wl.routing_w, extra_ug, extra_dn)
+    np.testing.assert_array_equal(r4.y, base.y)
+    sh = rng.permutation(wl.T)
+    r5 = orc.moe_expert_forward(wl.x[sh], wl.expert_ids[sh], wl.routing_w[sh], wl.w_ug, wl.w_down)
+    np.testing.assert_array_equal(r5.y, base.y[sh])
+
+
+def pin_f32_within_bound(orc) -> None:
+    """The float32 loop (the precision the method names for accumulation) and the float64 loop
+    round to the same bf16 values, except where a value lies within the float32 error bound
+    K*2^-24*sum|a_i b_i| of a rounding boundary: there U differs by one ulp, and H = SiLU(g)*u,
+    fed by two such U values, by at most two."""
+    wl = make_random(T=64, k=2, E=4, d=256, h=128, seed=41, drop_frac=0.05, w_sigma=0.05)
+    r64 = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, precision="f64")
+    r32 = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, precision="f32")
+    for name in ("h", "y_perm", "y"):
+        _assert_close_bits(getattr(r32, name), getattr(r64, name), f"f32 vs f64 {name}", min_exact=0.97, max_ulp=2)
+
+
+def pin_token_form(orc) -> None:
+    """The per-token form used for sampled checks equals the per-expert loop."""
+    wl = make_random(T=30, k=3, E=5, d=48, h=32, seed=51, drop_frac=0.1, w_sigma=0.1)
+    r = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
+    rows = np.stack([orc.token_forward(wl.x[t], wl.expert_ids[t], wl.routing_w[t], wl.w_ug, wl.w_down)
+                     for t in range(wl.T)])
+    _assert_close_bits(rows, r.y, "token form", min_exact=0.99, max_ulp=1)
+
+
+ALL_PINS = [
+    pin_toy_golden,
+    pin_printed_arithmetic,
+    pin_histogram_and_order,
+    pin_permute_unpermute_identity,
+    pin_single_expert_is_dense_mlp,
+    pin_column_partition,
+    pin_brute_force,
+    pin_invariances,
+    pin_f32_within_bound,
+    pin_token_form,
+]

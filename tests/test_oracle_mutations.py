@@ -1,0 +1,105 @@
+"""Planted mistakes in the oracle must be caught by at least one pin.
+
+Each case swaps one oracle function (on the CPU, in this process only) for a
+copy carrying a plausible mistake: a dropped term, a wrong sign, a wrong index,
+a transposed operand, a missing rounding point, an unstable order. The pins
+are then run; the case passes only if some pin rejects the mutated oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe as om
+from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
+from oracle_pins import ALL_PINS
+
+
+def _swiglu_variant(gate_up_swapped=False, round_u=True, use_up=True, transpose_down=False, silu_sign=1.0):
+    def f(a, w_ug, w_down, h, ft):
+        u_full = np.matmul(a, w_ug.T)
+        if round_u:
+            u_full = round_to_bf16(u_full)
+        g = u_full[:, :h].astype(ft)
+        u = u_full[:, h:].astype(ft)
+        if gate_up_swapped:
+            g, u = u, g
+        act = g / (ft(1) + np.exp(-silu_sign * g))
+        hid = round_to_bf16(act * u if use_up else act)
+        wd = w_down.T if transpose_down else w_down
+        return hid, round_to_bf16(np.matmul(hid.astype(ft), wd))
+    return f
+
+
+def _expert_forward_shifted(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision="f64"):
+    # wrong weight index: expert e multiplied by expert (e+1)'s weights
+    E = w_ug_bits.shape[0]
+    return _orig_expert_forward(x_perm_bits, offsets, np.roll(w_ug_bits, -1, axis=0),
+                                np.roll(w_down_bits, -1, axis=0), precision) if E > 1 else \
+        _orig_expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision)
+
+
+_orig_expert_forward = om.expert_forward
+_orig_stable = om.stable_route_order
+_orig_unpermute = om.unpermute
+
+
+def _reverse_within_expert(expert_ids, E, offsets):
+    perm, inv = _orig_stable(expert_ids, E, offsets)
+    offs = np.asarray(offsets)
+    for e in range(E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        perm[lo:hi] = perm[lo:hi][::-1].copy()
+    valid = inv >= 0
+    inv[np.asarray(perm[: int(offs[-1])])] = np.arange(int(offs[-1]), dtype=np.int32)
+    return perm, np.where(valid, inv, -1).astype(np.int32)
+
+
+def _hist_clip(expert_ids, E):
+    ids = np.asarray(expert_ids).reshape(-1)
+    ids = ids[ids >= 0]
+    return np.bincount(np.minimum(ids, E - 1), minlength=E).astype(np.int32)
+
+
+def _offsets_inclusive(counts):
+    c = np.cumsum(np.asarray(counts, dtype=np.int64))
+    return np.concatenate([c, c[-1:]]).astype(np.int32)
+
+
+def _unpermute_unweighted(y_perm_bits, inv, routing_w, T, k, precision="f64"):
+    return _orig_unpermute(y_perm_bits, inv, np.ones_like(np.asarray(routing_w)), T, k, precision)
+
+
+def _truncate_bf16(x):
+    x = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return ((x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)).astype(np.float64)
+
+
+MUTATIONS = {
+    "silu_sign": [("_swiglu_expert", _swiglu_variant(silu_sign=-1.0))],
+    "gate_up_swapped": [("_swiglu_expert", _swiglu_variant(gate_up_swapped=True))],
+    "u_not_rounded": [("_swiglu_expert", _swiglu_variant(round_u=False))],
+    "up_term_dropped": [("_swiglu_expert", _swiglu_variant(use_up=False))],
+    "down_transposed": [("_swiglu_expert", _swiglu_variant(transpose_down=True))],
+    "wrong_expert_weights": [("expert_forward", _expert_forward_shifted)],
+    "unstable_order": [("stable_route_order", _reverse_within_expert)],
+    "out_of_range_ids_counted": [("route_histogram", _hist_clip)],
+    "inclusive_offsets": [("exclusive_offsets", _offsets_inclusive)],
+    "weights_ignored": [("unpermute", _unpermute_unweighted)],
+    "truncating_rounding": [("round_to_bf16", _truncate_bf16)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    for attr, fn in MUTATIONS[name]:
+        monkeypatch.setattr(om, attr, fn)
+        if hasattr(oracle, attr):
+            monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(oracle)
+        except Exception as exc:  # AssertionError, or a shape error from a transposed operand
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"planted mistake {name!r} passed every pin"

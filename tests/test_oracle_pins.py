@@ -1,0 +1,11 @@
+"""The oracle against the pages' printed values, library routines, brute force and invariances."""
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin(oracle)
