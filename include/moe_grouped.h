@@ -1,0 +1,158 @@
+/*
+ * moe_grouped.h -- C ABI of the routed MoE expert step on MI355X (gfx950).
+ *
+ * The library runs the forward expert step of a routed mixture-of-experts
+ * layer on one GPU as three stream-ordered calls:
+ *
+ *   moe_permute            histogram of expert ids, exclusive scan into int32
+ *                          offsets, drop of invalid ids, stable order, inverse
+ *                          map and the permuted gather of token rows;
+ *   grouped_swiglu_expert  one persistent grouped GEMM over the ragged
+ *                          per-expert row blocks with SwiGLU fused into the
+ *                          gate/up projection, then the grouped down projection;
+ *   moe_unpermute          atomic-free gather + weighted reduction back to
+ *                          token order through the inverse map.
+ *
+ * Sources: "Section 09: Grouped GEMM" of the OLMo-core MoE report (Eq 13 for
+ * the expert, Figs 35-37 and Secs 9.2-9.4 for device-side offsets, fixed
+ * capacity buffers and unpadded compute) and the halo toolkit's "Grouped GEMM"
+ * notes (dropping ids outside [0, E) before the sort, int32 cumulative
+ * offsets, the sentinel-padded inverse map used for an atomic-free
+ * scatter-back, gate-then-up weight chunks).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is a DEVICE pointer on the current HIP device. bf16
+ *   values are passed as uint16_t bit patterns. Every tensor is dense and
+ *   row-major with the shape given next to it.
+ * - The caller allocates and frees every buffer. The library keeps no state
+ *   between calls beyond per-device properties it caches on first use.
+ * - Calls are asynchronous on `stream`: no call synchronises, copies a count
+ *   to the host or allocates. Row counts exist only as device data.
+ * - Shapes are capacity shapes: S = T*k dispatch slots; x_perm, h_buf and
+ *   y_perm have S rows whatever the routing, and only their first
+ *   M = offsets[E] rows are written (rows >= M and perm[M..S) are left as they
+ *   were). Dispatch slot s = t*k + j is token t's j-th routed expert.
+ * - A pointer may be NULL only when its tensor has zero elements.
+ * - Return values are host-side validation and launch results. Nothing is
+ *   ever reported from the device: invalid expert ids are data, and are
+ *   dropped. Status codes are listed in moe_status.
+ * - Calls on different streams are independent and thread-safe.
+ */
+#ifndef MOE_GROUPED_H_
+#define MOE_GROUPED_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_EXPERTS 1024
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL_POINTER = 1,       /* a pointer is NULL while its tensor is non-empty           */
+  MOE_ERR_BAD_SHAPE = 2,          /* T<0, k<1, E<1 or E>1024, d or h < 8 or not a multiple of 8,
+                                     T*k >= 2^31, or cap_rows < 0                               */
+  MOE_ERR_MISALIGNED = 3,         /* a bf16 tensor not 16-byte aligned, or an int32/float
+                                     tensor not 4-byte aligned                                  */
+  MOE_ERR_WORKSPACE = 4,          /* workspace_bytes < moe_permute_workspace_bytes(T, k, E)     */
+  MOE_ERR_UNSUPPORTED_DEVICE = 5, /* the current HIP device is not gfx950, or no device         */
+  MOE_ERR_LAUNCH = 6              /* a HIP error was reported while launching                    */
+} moe_status;
+
+/* Bytes of device workspace moe_permute needs for T tokens, k slots per token
+ * and E experts (a per-chunk histogram table). Pure host arithmetic; returns 0
+ * for invalid shapes. */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
+
+/* Dispatch preparation (OLMo report Sec 9.2-9.3 and Fig 37; halo notes on the
+ * expert step and on the inverse map).
+ *
+ *   x           bf16  [T, d]  token rows
+ *   expert_ids  int32 [T, k]  routed expert of each slot; any id outside
+ *                             [0, E) (such as the -1 padding of an expert-
+ *                             parallel dispatch) marks a dropped slot
+ *   x_perm      bf16  [T*k, d] out: rows [0, M) hold X[perm[p] / k]
+ *   counts      int32 [E]     out: kept slots per expert
+ *   offsets     int32 [E+1]   out: offsets[0] = 0, offsets[e+1] =
+ *                             offsets[e] + counts[e]; expert e owns sorted
+ *                             rows [offsets[e], offsets[e+1]); M = offsets[E]
+ *   perm        int32 [T*k]   out: perm[p] = slot in sorted row p, p < M
+ *   inv_map     int32 [T, k]  out: sorted row of each slot, -1 if dropped
+ *   workspace   device scratch of at least moe_permute_workspace_bytes(T,k,E)
+ *
+ * Inside an expert's block, slots keep ascending slot order (the order of a
+ * stable sort by expert id), so counts, offsets, perm[0, M) and inv_map are
+ * fully determined by expert_ids. T = 0 is valid (counts and offsets become
+ * zeros). */
+moe_status moe_permute(const uint16_t* x, const int32_t* expert_ids, int64_t T, int32_t k, int64_t d,
+                       int32_t E, uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_map, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Grouped SwiGLU expert (OLMo report Eq 13 and Sec 9.2's device-scheduled
+ * grouped GEMM). For every expert e with rows [offsets[e], offsets[e+1]):
+ *
+ *   U_e = x_perm[rows] * W_ug[e]^T          bf16 inputs, fp32 accumulation,
+ *                                           rounded to bf16 (round-to-nearest-even)
+ *   H_e = bf16( SiLU(U_e[:, :h]) * U_e[:, h:] )      written to h_buf[rows]
+ *   Y_e = bf16( H_e * W_down[e] )                    written to y_perm[rows]
+ *
+ *   x_perm   bf16  [cap_rows, d]
+ *   offsets  int32 [E+1]       device offsets as written by moe_permute; they
+ *                              are clamped to [0, cap_rows] and made monotone
+ *                              on the device, so no row outside the buffers is
+ *                              ever touched
+ *   w_ug     bf16  [E, 2h, d]  gate rows [0, h), up rows [h, 2h)
+ *   w_down   bf16  [E, h, d]
+ *   h_buf    bf16  [cap_rows, h] out (the SwiGLU activations)
+ *   y_perm   bf16  [cap_rows, d] out
+ *
+ * Empty experts cost nothing; K need not be a multiple of the K tile; rows
+ * past M are never computed. Equivalent to moe_gemm_up_swiglu followed by
+ * moe_gemm_down on the same stream. */
+moe_status grouped_swiglu_expert(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                 const uint16_t* w_down, int64_t cap_rows, int64_t d, int64_t h, int32_t E,
+                                 uint16_t* h_buf, uint16_t* y_perm, hipStream_t stream);
+
+/* The first half of grouped_swiglu_expert alone: one kernel launch that
+ * writes h_buf[rows] = bf16(SiLU(bf16(g)) * bf16(u)) with [g | u] =
+ * x_perm[rows] * W_ug[e]^T. Arguments as above. */
+moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                              int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
+                              hipStream_t stream);
+
+/* The second half alone: one kernel launch that writes y_perm[rows] =
+ * bf16(h_buf[rows] * W_down[e]). Arguments as above. */
+moe_status moe_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down,
+                         int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* y_perm,
+                         hipStream_t stream);
+
+/* Atomic-free scatter-back (halo notes: the inverse map turns the scatter
+ * into a gather plus a reduction; routing weights are applied here).
+ *
+ *   y_perm     bf16  [T*k, d]
+ *   inv_map    int32 [T, k]   sorted row of each slot; entries outside
+ *                             [0, T*k) (such as -1) are skipped
+ *   routing_w  fp32  [T, k]
+ *   y          bf16  [T, d]   out: y[t] = bf16( sum over kept j, ascending,
+ *                             of routing_w[t,j] * y_perm[inv_map[t,j]] ),
+ *                             accumulated in fp32; a token with no kept slot
+ *                             gets a zero row
+ *
+ * Every row of y is written. Weights are not renormalised over kept slots. */
+moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const float* routing_w, int64_t T,
+                         int32_t k, int64_t d, uint16_t* y, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GROUPED_H_ */

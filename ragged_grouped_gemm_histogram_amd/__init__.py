@@ -1,0 +1,224 @@
+"""Python binding of libmoe_grouped, the routed MoE expert step on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP library's kernels. torch
+supplies device memory and the current stream. The functions mirror the C ABI
+declared in ``include/moe_grouped.h``; the optional ``out=`` tensors let a
+caller keep fixed capacity-shaped buffers across calls.
+
+The library must have been built (``python -m ragged_grouped_gemm_histogram_amd.build``);
+every call raises ImportError when it is missing. There is no other code path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_grouped.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_grouped.h")
+MAX_EXPERTS = 1024
+
+MOE_OK = 0
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGNATURES = {
+    "moe_permute_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "grouped_swiglu_expert": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "moe_gemm_up_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_gemm_down": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_unpermute": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+_LIB = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmoe_grouped.so (once). Raises ImportError when it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m ragged_grouped_gemm_histogram_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {load_library().moe_status_string(status).decode()}")
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/moe_grouped.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return re.findall(r"^\s*(?:moe_status|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def _check(status: int, call: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, call)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _want(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(t, name, dtype, shape, device):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _want(t, name, dtype, shape, device)
+
+
+@dataclass
+class Permuted:
+    x_perm: torch.Tensor  # bf16 [T*k, d]; rows [0, M) valid
+    counts: torch.Tensor  # int32 [E]
+    offsets: torch.Tensor  # int32 [E+1]
+    perm: torch.Tensor  # int32 [T*k]; entries [0, M) valid
+    inv_map: torch.Tensor  # int32 [T, k]; -1 for dropped slots
+
+
+def permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(load_library().moe_permute_workspace_bytes(T, k, E))
+
+
+def moe_permute(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int, *, x_perm=None, counts=None,
+                offsets=None, perm=None, inv_map=None, workspace=None) -> Permuted:
+    """Histogram, offsets, stable order, inverse map and permuted gather (one stream, no sync)."""
+    if x.dim() != 2 or expert_ids.dim() != 2:
+        raise ValueError("x must be [T, d] and expert_ids [T, k]")
+    T, d = x.shape
+    k = expert_ids.shape[1]
+    dev = x.device
+    _want(x, "x", torch.bfloat16, (T, d), dev)
+    _want(expert_ids, "expert_ids", torch.int32, (T, k), dev)
+    S = T * k
+    E = int(num_experts)
+    x_perm = _out(x_perm, "x_perm", torch.bfloat16, (S, d), dev)
+    counts = _out(counts, "counts", torch.int32, (E,), dev)
+    offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
+    perm = _out(perm, "perm", torch.int32, (S,), dev)
+    inv_map = _out(inv_map, "inv_map", torch.int32, (T, k), dev)
+    need = permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4),), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    _check(load_library().moe_permute(_ptr(x), _ptr(expert_ids), T, k, d, E, _ptr(x_perm), _ptr(counts), _ptr(offsets),
+                           _ptr(perm), _ptr(inv_map), _ptr(workspace), workspace.numel(), _stream(x)),
+           "moe_permute")
+    return Permuted(x_perm, counts, offsets, perm, inv_map)
+
+
+def _gemm_shapes(a: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor):
+    if a.dim() != 2 or w.dim() != 3 or offsets.dim() != 1:
+        raise ValueError("expected a 2-D activation buffer, 1-D offsets and 3-D expert weights")
+    return a.shape[0], a.device
+
+
+def moe_gemm_up_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.Tensor, *, h_buf=None) -> torch.Tensor:
+    """h_buf[rows_e] = bf16(SiLU(bf16(G)) * bf16(U)), [G|U] = x_perm[rows_e] @ W_ug[e]^T (one launch)."""
+    cap, dev = _gemm_shapes(x_perm, offsets, w_ug)
+    E, two_h, d = w_ug.shape
+    h = two_h // 2
+    _want(x_perm, "x_perm", torch.bfloat16, (cap, d), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w_ug, "w_ug", torch.bfloat16, (E, 2 * h, d), dev)
+    h_buf = _out(h_buf, "h_buf", torch.bfloat16, (cap, h), dev)
+    _check(load_library().moe_gemm_up_swiglu(_ptr(x_perm), _ptr(offsets), _ptr(w_ug), cap, d, h, E, _ptr(h_buf),
+                                  _stream(x_perm)), "moe_gemm_up_swiglu")
+    return h_buf
+
+
+def moe_gemm_down(h_buf: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, *, y_perm=None) -> torch.Tensor:
+    """y_perm[rows_e] = bf16(h_buf[rows_e] @ W_down[e]) (one launch)."""
+    cap, dev = _gemm_shapes(h_buf, offsets, w_down)
+    E, h, d = w_down.shape
+    _want(h_buf, "h_buf", torch.bfloat16, (cap, h), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w_down, "w_down", torch.bfloat16, (E, h, d), dev)
+    y_perm = _out(y_perm, "y_perm", torch.bfloat16, (cap, d), dev)
+    _check(load_library().moe_gemm_down(_ptr(h_buf), _ptr(offsets), _ptr(w_down), cap, d, h, E, _ptr(y_perm), _stream(h_buf)),
+           "moe_gemm_down")
+    return y_perm
+
+
+def grouped_swiglu_expert(x_perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.Tensor, w_down: torch.Tensor, *,
+                          h_buf=None, y_perm=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Eq 13 for every expert's row block: returns (h_buf, y_perm), both [cap, *] with rows [0, M) valid."""
+    cap, dev = _gemm_shapes(x_perm, offsets, w_ug)
+    E, two_h, d = w_ug.shape
+    h = two_h // 2
+    _want(x_perm, "x_perm", torch.bfloat16, (cap, d), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w_ug, "w_ug", torch.bfloat16, (E, 2 * h, d), dev)
+    _want(w_down, "w_down", torch.bfloat16, (E, h, d), dev)
+    h_buf = _out(h_buf, "h_buf", torch.bfloat16, (cap, h), dev)
+    y_perm = _out(y_perm, "y_perm", torch.bfloat16, (cap, d), dev)
+    _check(load_library().grouped_swiglu_expert(_ptr(x_perm), _ptr(offsets), _ptr(w_ug), _ptr(w_down), cap, d, h, E,
+                                     _ptr(h_buf), _ptr(y_perm), _stream(x_perm)), "grouped_swiglu_expert")
+    return h_buf, y_perm
+
+
+def moe_unpermute(y_perm: torch.Tensor, inv_map: torch.Tensor, routing_w: torch.Tensor, *, y=None) -> torch.Tensor:
+    """y[t] = bf16(sum_j w[t,j] * y_perm[inv_map[t,j]]) over kept slots (atomic-free gather + reduce)."""
+    if inv_map.dim() != 2:
+        raise ValueError("inv_map must be [T, k]")
+    T, k = inv_map.shape
+    dev = y_perm.device
+    d = y_perm.shape[1]
+    _want(y_perm, "y_perm", torch.bfloat16, (T * k, d), dev)
+    _want(inv_map, "inv_map", torch.int32, (T, k), dev)
+    _want(routing_w, "routing_w", torch.float32, (T, k), dev)
+    y = _out(y, "y", torch.bfloat16, (T, d), dev)
+    _check(load_library().moe_unpermute(_ptr(y_perm), _ptr(inv_map), _ptr(routing_w), T, k, d, _ptr(y), _stream(y_perm)),
+           "moe_unpermute")
+    return y
+
+
+def moe_expert_forward(x, expert_ids, routing_w, w_ug, w_down):
+    """The whole step: permute, grouped SwiGLU expert, unpermute. Returns (y, Permuted, h_buf, y_perm)."""
+    p = moe_permute(x, expert_ids, w_ug.shape[0])
+    h_buf, y_perm = grouped_swiglu_expert(p.x_perm, p.offsets, w_ug, w_down)
+    y = moe_unpermute(y_perm, p.inv_map, routing_w)
+    return y, p, h_buf, y_perm
+
+
+__all__ = [
+    "LIB_PATH", "MAX_EXPERTS", "MoeError", "Permuted", "grouped_swiglu_expert", "header_functions", "load_library",
+    "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu", "moe_permute", "moe_unpermute",
+    "permute_workspace_bytes",
+]

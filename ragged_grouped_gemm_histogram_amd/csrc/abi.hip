@@ -1,0 +1,155 @@
+// C ABI of the MoE expert step: host-side validation, device check and launches.
+// Nothing here allocates, synchronises or reads device data.
+
+#include <atomic>
+#include <cstring>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_cus[kMaxDevices];
+
+constexpr int64_t kMaxSlots = (int64_t(1) << 31) - 1;  // int32 row indices and offsets
+
+bool load_props(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  if (g_arch[dev].load(std::memory_order_acquire) != 0) return true;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+  g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+  g_arch[dev].store(std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1, std::memory_order_release);
+  return true;
+}
+
+moe_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !load_props(dev)) return MOE_ERR_UNSUPPORTED_DEVICE;
+  return g_arch[dev].load(std::memory_order_acquire) == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+inline bool missing(const void* p, int64_t elems) { return elems > 0 && p == nullptr; }
+inline bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+inline bool bad_width(int64_t w) { return w < 8 || (w % 8) != 0 || w > (int64_t(1) << 24); }
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+moe_status check_gemm_shape(int64_t cap_rows, int64_t d, int64_t h, int32_t E) {
+  if (cap_rows < 0 || cap_rows > kMaxSlots || bad_width(d) || bad_width(h) || E < 1 || E > MOE_MAX_EXPERTS)
+    return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+int device_cu_count(int dev) {
+  if (!load_props(dev)) return 256;
+  const int n = g_cus[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 256;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS || T > kMaxSlots / k) return 0;
+  return (size_t)permute_chunks(T * k) * (size_t)E * sizeof(int32_t);
+}
+
+moe_status moe_permute(const uint16_t* x, const int32_t* expert_ids, int64_t T, int32_t k, int64_t d, int32_t E,
+                       uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_map,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS || bad_width(d) || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  if (missing(x, T * d) || missing(expert_ids, S) || missing(x_perm, S * d) || missing(counts, E) ||
+      missing(offsets, E + 1) || missing(perm, S) || missing(inv_map, S) || missing(workspace, (int64_t)need))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x, 16) || misaligned(x_perm, 16) || misaligned(expert_ids, 4) || misaligned(counts, 4) ||
+      misaligned(offsets, 4) || misaligned(perm, 4) || misaligned(inv_map, 4) || misaligned(workspace, 4))
+    return MOE_ERR_MISALIGNED;
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  const moe_status dev = check_device();
+  if (dev != MOE_OK) return dev;
+  (void)hipGetLastError();
+  return launched(launch_permute(x, expert_ids, T, k, d, E, x_perm, counts, offsets, perm, inv_map,
+                                 static_cast<int32_t*>(workspace), stream));
+}
+
+moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug, int64_t cap_rows,
+                              int64_t d, int64_t h, int32_t E, uint16_t* h_buf, hipStream_t stream) {
+  moe_status st = check_gemm_shape(cap_rows, d, h, E);
+  if (st != MOE_OK) return st;
+  if (missing(x_perm, cap_rows * d) || missing(offsets, E + 1) || missing(w_ug, (int64_t)E * 2 * h * d) ||
+      missing(h_buf, cap_rows * h))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x_perm, 16) || misaligned(w_ug, 16) || misaligned(h_buf, 16) || misaligned(offsets, 4))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_gemm_up_swiglu(x_perm, offsets, w_ug, cap_rows, d, h, E, h_buf, stream));
+}
+
+moe_status moe_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down, int64_t cap_rows,
+                         int64_t d, int64_t h, int32_t E, uint16_t* y_perm, hipStream_t stream) {
+  moe_status st = check_gemm_shape(cap_rows, d, h, E);
+  if (st != MOE_OK) return st;
+  if (missing(h_buf, cap_rows * h) || missing(offsets, E + 1) || missing(w_down, (int64_t)E * h * d) ||
+      missing(y_perm, cap_rows * d))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(h_buf, 16) || misaligned(w_down, 16) || misaligned(y_perm, 16) || misaligned(offsets, 4))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_gemm_down(h_buf, offsets, w_down, cap_rows, d, h, E, y_perm, stream));
+}
+
+moe_status grouped_swiglu_expert(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                 const uint16_t* w_down, int64_t cap_rows, int64_t d, int64_t h, int32_t E,
+                                 uint16_t* h_buf, uint16_t* y_perm, hipStream_t stream) {
+  moe_status st = check_gemm_shape(cap_rows, d, h, E);
+  if (st != MOE_OK) return st;
+  if (missing(w_down, (int64_t)E * h * d) || missing(y_perm, cap_rows * d)) return MOE_ERR_NULL_POINTER;
+  if (misaligned(w_down, 16) || misaligned(y_perm, 16)) return MOE_ERR_MISALIGNED;
+  st = moe_gemm_up_swiglu(x_perm, offsets, w_ug, cap_rows, d, h, E, h_buf, stream);
+  if (st != MOE_OK) return st;
+  return moe_gemm_down(h_buf, offsets, w_down, cap_rows, d, h, E, y_perm, stream);
+}
+
+moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const float* routing_w, int64_t T, int32_t k,
+                         int64_t d, uint16_t* y, hipStream_t stream) {
+  if (T < 0 || k < 1 || bad_width(d) || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  if (missing(y_perm, S * d) || missing(inv_map, S) || missing(routing_w, S) || missing(y, T * d))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(y_perm, 16) || misaligned(y, 16) || misaligned(inv_map, 4) || misaligned(routing_w, 4))
+    return MOE_ERR_MISALIGNED;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_unpermute(y_perm, inv_map, routing_w, T, k, d, y, stream));
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL_POINTER: return "MOE_ERR_NULL_POINTER: a pointer is NULL while its tensor is non-empty";
+    case MOE_ERR_BAD_SHAPE: return "MOE_ERR_BAD_SHAPE: a size is out of range (T, k, E, d, h or T*k)";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: a bf16 tensor is not 16-byte aligned or an int32/fp32 tensor not 4-byte aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_permute_workspace_bytes()";
+    case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE: the current HIP device is not gfx950";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: a kernel launch reported a HIP error";
+  }
+  return "unknown moe_status";
+}
+
+}  // extern "C"

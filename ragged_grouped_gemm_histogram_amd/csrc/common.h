@@ -1,0 +1,63 @@
+// Shared device helpers and host-side launch declarations for the MoE expert step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "moe_grouped.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- device side
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bit pattern, round to nearest even (the compiler lowers the
+// __bf16 conversion to the gfx950 hardware convert, which rounds to nearest even).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __builtin_bit_cast(float, b16 << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------ host side
+
+// Number of compute units of a device (cached per device).
+int device_cu_count(int dev);
+
+inline int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  return dev;
+}
+
+// Permute: chunking of the dispatch slots for the per-chunk histogram table.
+constexpr int kPermuteChunk = 256;  // slots per chunk (one wave walks it in 4 steps of 64)
+inline int64_t permute_chunks(int64_t S) { return (S + kPermuteChunk - 1) / kPermuteChunk; }
+
+hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int32_t k, int64_t d, int32_t E,
+                          uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          int32_t* table, hipStream_t stream);
+
+hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                 int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
+                                 hipStream_t stream);
+
+hipError_t launch_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down,
+                            int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* y_perm,
+                            hipStream_t stream);
+
+hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* inv, const float* w, int64_t T, int32_t k,
+                            int64_t d, uint16_t* y, hipStream_t stream);
+
+}  // namespace moe

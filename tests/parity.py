@@ -22,6 +22,15 @@ RTOL = 1e-2
 REL_L2 = 1e-2
 REL_MAX = 1e-2
 
+# The stored SwiGLU activations H = bf16(SiLU(g) * u) are formed from two values
+# that were themselves rounded to bf16 (g and u, the halves of U). An fp32
+# accumulation order different from the reference's can leave g and u each one
+# bf16 step (at most 2^-7 relative) from the reference's, and H's own rounding
+# adds another step; where SiLU(g) is large (g > 0) the three add up to
+# 3 * 2^-7 relative. For g < 0 the relative sensitivity grows like |g| but
+# |SiLU(g)| < 0.28, so the absolute bound covers it. y keeps the contract bound.
+RTOL_H = 3 * 2.0**-7
+
 
 def bf16_to_f64(bits) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16)

@@ -1,0 +1,117 @@
+"""The C ABI on a host without a GPU: symbols, workspace arithmetic, host-side validation.
+
+No call here reaches a kernel: every case returns from host validation before
+any device work, and the device check itself is exercised on a host with no
+GPU (it must report MOE_ERR_UNSUPPORTED_DEVICE, not crash).
+"""
+
+import ctypes
+
+import pytest
+import torch
+
+import ragged_grouped_gemm_histogram_amd as moe
+
+OK, NULLP, SHAPE, ALIGN, WS, DEV, LAUNCH = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load_library()
+
+
+def test_exports_every_header_symbol(lib):
+    names = moe.header_functions()
+    assert set(names) >= {"moe_permute", "grouped_swiglu_expert", "moe_unpermute", "moe_permute_workspace_bytes",
+                          "moe_gemm_up_swiglu", "moe_gemm_down", "moe_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.moe_status_string(s).decode().startswith("MOE_")
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def test_workspace_bytes(lib):
+    f = moe.permute_workspace_bytes
+    assert f(0, 1, 4) == 0
+    assert f(10, 1, 4) == 1 * 4 * 4  # one chunk of 256 slots, 4 experts, int32
+    assert f(8192, 8, 64) == (65536 // 256) * 64 * 4
+    assert f(257, 1, 3) == 2 * 3 * 4
+    assert f(-1, 1, 4) == 0 and f(1, 0, 4) == 0 and f(1, 1, 0) == 0 and f(1, 1, 1025) == 0
+    assert f(2**31, 1, 4) == 0  # T*k must stay below 2^31
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation first
+
+
+def permute(lib, T=4, k=2, d=8, E=4, x=FAKE, ids=FAKE, xp=FAKE, counts=FAKE, offs=FAKE, perm=FAKE, inv=FAKE,
+            ws=FAKE, wsb=1 << 20):
+    return lib.moe_permute(x, ids, T, k, d, E, xp, counts, offs, perm, inv, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(E=0), SHAPE), (dict(E=1025), SHAPE), (dict(d=12), SHAPE),
+    (dict(d=0), SHAPE), (dict(T=2**31, k=1), SHAPE), (dict(T=2**30, k=2), SHAPE),
+    (dict(x=None), NULLP), (dict(ids=None), NULLP), (dict(xp=None), NULLP), (dict(counts=None), NULLP),
+    (dict(offs=None), NULLP), (dict(perm=None), NULLP), (dict(inv=None), NULLP), (dict(ws=None), NULLP),
+    (dict(x=FAKE + 8), ALIGN), (dict(xp=FAKE + 2), ALIGN), (dict(ids=FAKE + 2), ALIGN), (dict(inv=FAKE + 1), ALIGN),
+    (dict(wsb=3), WS),
+])
+def test_permute_validation(lib, kw, status):
+    assert permute(lib, **kw) == status
+
+
+def test_permute_empty_tensors_may_be_null(lib):
+    # T = 0: every slot tensor is empty, so NULL is fine; only offsets/counts (E entries) are required.
+    st = permute(lib, T=0, x=None, ids=None, xp=None, perm=None, inv=None, ws=None, wsb=0)
+    assert st in (OK, DEV)  # no GPU here: validation passes, then the device check reports
+    assert permute(lib, T=0, x=None, ids=None, xp=None, perm=None, inv=None, ws=None, wsb=0, counts=None) == NULLP
+
+
+def gemm(lib, fn, cap=16, d=16, h=16, E=2, a=FAKE, offs=FAKE, w=FAKE, out=FAKE):
+    return getattr(lib, fn)(a, offs, w, cap, d, h, E, out, None)
+
+
+@pytest.mark.parametrize("fn", ["moe_gemm_up_swiglu", "moe_gemm_down"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=-1), SHAPE), (dict(d=4), SHAPE), (dict(h=20), SHAPE), (dict(E=0), SHAPE), (dict(E=2000), SHAPE),
+    (dict(a=None), NULLP), (dict(offs=None), NULLP), (dict(w=None), NULLP), (dict(out=None), NULLP),
+    (dict(a=FAKE + 4), ALIGN), (dict(w=FAKE + 8), ALIGN), (dict(out=FAKE + 2), ALIGN), (dict(offs=FAKE + 2), ALIGN),
+])
+def test_gemm_validation(lib, fn, kw, status):
+    assert gemm(lib, fn, **kw) == status
+
+
+def test_grouped_validation_checks_both_halves(lib):
+    f = lib.grouped_swiglu_expert
+    assert f(FAKE, FAKE, FAKE, None, 16, 16, 16, 2, FAKE, FAKE, None) == NULLP  # w_down
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 16, 16, 2, FAKE, None, None) == NULLP  # y_perm
+    assert f(FAKE, FAKE, FAKE, FAKE + 2, 16, 16, 16, 2, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 12, 16, 2, FAKE, FAKE, None) == SHAPE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(d=6), SHAPE),
+    (dict(yp=None), NULLP), (dict(inv=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP),
+    (dict(yp=FAKE + 2), ALIGN), (dict(y=FAKE + 8), ALIGN), (dict(w=FAKE + 2), ALIGN),
+])
+def test_unpermute_validation(lib, kw, status):
+    a = dict(yp=FAKE, inv=FAKE, w=FAKE, T=4, k=2, d=8, y=FAKE)
+    a.update(kw)
+    assert lib.moe_unpermute(a["yp"], a["inv"], a["w"], a["T"], a["k"], a["d"], a["y"], None) == status
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour on a host without a GPU")
+def test_device_check_without_gpu(lib):
+    assert permute(lib) == DEV
+    assert gemm(lib, "moe_gemm_down") == DEV
+    assert lib.moe_unpermute(FAKE, FAKE, FAKE, 4, 2, 8, FAKE, None) == DEV
+
+
+def test_binding_rejects_bad_tensors():
+    x = torch.zeros((4, 8), dtype=torch.float32)
+    with pytest.raises((TypeError, ValueError)):
+        moe.moe_permute(x, torch.zeros((4, 2), dtype=torch.int32), 4)
