@@ -10,24 +10,30 @@
 // rebuilds the problem list from the device offsets in LDS (expert e owns
 // sorted rows [offsets[e], offsets[e+1]); its pointers are affine in e and
 // offsets[e]), then takes output tiles in a static round-robin until none is
-// left. Empty experts contribute no tile; rows past an expert's block, columns
-// past N and the K remainder are masked with zeros on load and skipped on
-// store.
+// left. Empty experts contribute no tile; rows past an expert's block and
+// columns past N are never stored.
 //
-// Tile: BM rows x BN weight rows, K stepped by 64 through double-buffered LDS
-// (global -> registers -> LDS while the previous stage feeds the MFMAs).
-// 4 waves in a 2x2 grid, each owning (BM/2) x (BN/2) outputs as 32x32 blocks
-// of v_mfma_f32_32x32x16_bf16. The MFMA is issued with the weight fragment as
-// its first operand, so each lane ends up holding four consecutive output
-// columns of one output row; the epilogue packs them to bf16, stages the tile
-// through LDS and writes whole 16-byte chunks.
+// Tile: BM rows x BN weight rows, K stepped by 64. 4 waves in a 2x2 grid, each
+// owning (BM/2) x (BN/2) outputs as 32x32 blocks of v_mfma_f32_32x32x16_bf16.
+// The MFMA takes the weight fragment as its first operand, so each lane ends
+// up holding four consecutive output columns of one output row; the epilogue
+// packs them to bf16, stages the tile through LDS and writes 16-byte chunks.
 //
 // For the up projection the BN weight rows of a tile are BN/2 gate rows
 // followed by the BN/2 matching up rows (W_ug is gate-then-up, chunked), so a
 // lane holds each gate value and its up value in the same register slot and
-// SwiGLU is applied in registers. For the down projection W_down [h, d] is
-// N-contiguous: each thread loads an 8(k) x 8(n) block and transposes it in
-// registers so that LDS always holds K-contiguous rows.
+// SwiGLU is applied in registers.
+//
+// Two main loops share that structure:
+//  * pipelined (K % 64 == 0, every realistic width): global -> LDS direct
+//    loads (global_load_lds_dwordx4) into a 3-stage ring, two stages in flight
+//    while the third feeds the MFMAs, one barrier per K step, no staging
+//    registers. W_down [h, d] is N-contiguous; its tiles land in LDS as they
+//    are in memory and the MFMA fragments are read with the gfx950 LDS
+//    transpose read (ds_read_b64_tr_b16).
+//  * register-staged (any K % 8 == 0): global -> registers -> LDS with zero
+//    fill for the K remainder, double-buffered; W_down blocks of 8(k) x 8(n)
+//    are transposed in registers.
 
 #include "common.h"
 
@@ -38,6 +44,10 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int BK = 64;         // K per stage: 8 chunks of 16 bytes per tile row
 constexpr int kChunksK = BK / 8;
 constexpr int kGroupM = 8;     // m-tiles per group in the tile order (operand reuse in L2)
+constexpr int kStages = 3;     // LDS ring depth of the pipelined loop
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 template <int BM, int BN, bool GATED>
 struct Tile {
@@ -47,13 +57,45 @@ struct Tile {
   static constexpr int OUT_CPR = OUTW / 8;          // 16-byte chunks per output row
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int A_LOADS = BM * kChunksK / kThreads;  // 16-byte chunks per thread per stage
+  static constexpr int A_LOADS = BM * kChunksK / kThreads;  // register path: 16-byte chunks per thread
   static constexpr int B_LOADS = BN * kChunksK / kThreads;
+  static constexpr int A_OPS = A_BYTES / 1024 / 4;  // pipelined path: 1 KB wave loads per wave per stage
+  static constexpr int B_OPS = B_BYTES / 1024 / 4;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 32x32 blocks over a 2x2 wave grid");
-  static_assert(BM * OUTW * 2 <= LDS_BYTES, "epilogue tile must fit in the stage buffers");
+  static_assert(BM * OUTW * 2 <= 2 * STAGE_BYTES, "epilogue tile must fit in the stage buffers");
   static_assert((OUT_CPR & (OUT_CPR - 1)) == 0, "output chunk count must be a power of two");
   static_assert(!GATED || FN % 2 == 0, "gated tiles pair gate and up blocks");
+};
+
+struct GemmArgs {
+  const uint16_t* A;        // activations [cap_rows, K], row pitch lda
+  int64_t lda;
+  const uint16_t* W;        // expert weights
+  int64_t w_expert_stride;  // elements between experts
+  int64_t ldw;              // row pitch of a weight matrix
+  int64_t gate_up_rows;     // gated: row offset of the up block (h); unused otherwise
+  int64_t N;                // output columns
+  int64_t K;
+  const int32_t* offsets;   // [E+1]
+  int E;
+  int64_t cap_rows;
+  uint16_t* out;            // [cap_rows, N], row pitch ldo
+  int64_t ldo;
+};
+
+struct ProblemList {
+  int seg_lo[MOE_MAX_EXPERTS];
+  int seg_rows[MOE_MAX_EXPERTS];
+  int mt_prefix[MOE_MAX_EXPERTS + 1];
+  int scan_tmp[kThreads];
+};
+
+struct TileCoord {
+  int e;
+  int mi;
+  int64_t row0;     // first sorted row of the tile
+  int rows_valid;   // rows of the tile inside the expert's block
+  int64_t n0;       // first output column
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
@@ -64,6 +106,22 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(a, b, 0x05040100u); }
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(a, b, 0x07060302u); }
 
+// One 16-byte chunk per lane from `src` into LDS[lds_addr + 16 * lane] (M0 holds the wave's LDS base).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
 // Map a persistent workgroup to a logical worker so that consecutive logical
 // workers (which take consecutive tiles) sit on one XCD: workgroups are
 // dealt to the 8 XCDs round-robin.
@@ -73,24 +131,11 @@ __device__ __forceinline__ int logical_worker() {
   return (b % 8) * (G / 8) + b / 8;
 }
 
-template <int BM, int BN, bool GATED, bool B_NMAJOR>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t w_expert_stride,
-    int64_t ldw, int64_t gate_up_rows, int64_t N, int64_t K, const int32_t* __restrict__ offsets, int E,
-    int64_t cap_rows, uint16_t* __restrict__ out, int64_t ldo) {
-  using C = Tile<BM, BN, GATED>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int seg_lo[MOE_MAX_EXPERTS];
-  __shared__ int seg_rows[MOE_MAX_EXPERTS];
-  __shared__ int mt_prefix[MOE_MAX_EXPERTS + 1];
-  __shared__ int scan_tmp[kThreads];
-
+// Problem list from the device offsets, clamped so no access leaves the buffers:
+// per expert its first row, its row count and the prefix of its m-tile counts.
+template <int BM>
+__device__ void build_problem_list(const GemmArgs& g, ProblemList& pl) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- problem list from the device offsets (clamped: no access outside the buffers)
   constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
   int mt_local[kPer];
   int sum = 0;
@@ -98,67 +143,321 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (int i = 0; i < kPer; ++i) {
     const int e = tid * kPer + i;
     int mt = 0;
-    if (e < E) {
-      int64_t lo = offsets[e], hi = offsets[e + 1];
-      lo = lo < 0 ? 0 : (lo > cap_rows ? cap_rows : lo);
-      hi = hi < lo ? lo : (hi > cap_rows ? cap_rows : hi);
-      seg_lo[e] = (int)lo;
-      seg_rows[e] = (int)(hi - lo);
+    if (e < g.E) {
+      int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
+      lo = lo < 0 ? 0 : (lo > g.cap_rows ? g.cap_rows : lo);
+      hi = hi < lo ? lo : (hi > g.cap_rows ? g.cap_rows : hi);
+      pl.seg_lo[e] = (int)lo;
+      pl.seg_rows[e] = (int)(hi - lo);
       mt = (int)((hi - lo + BM - 1) / BM);
     }
     mt_local[i] = mt;
     sum += mt;
   }
-  scan_tmp[tid] = sum;
+  pl.scan_tmp[tid] = sum;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? scan_tmp[tid - off] : 0;
+    const int add = tid >= off ? pl.scan_tmp[tid - off] : 0;
     __syncthreads();
-    scan_tmp[tid] += add;
+    pl.scan_tmp[tid] += add;
     __syncthreads();
   }
-  {
-    int run = scan_tmp[tid] - sum;
+  int run = pl.scan_tmp[tid] - sum;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = tid * kPer + i;
-      if (e < E) mt_prefix[e] = run;
-      run += mt_local[i];
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid * kPer + i;
+    if (e < g.E) pl.mt_prefix[e] = run;
+    run += mt_local[i];
+  }
+  if (tid == kThreads - 1) pl.mt_prefix[g.E] = pl.scan_tmp[kThreads - 1];
+  __syncthreads();
+}
+
+// Tile t -> (expert, m-tile, n-tile). Groups of kGroupM consecutive m-tiles
+// sweep every n-tile before the next group starts, so tiles that run at the
+// same time share A rows and weight rows.
+template <int BM, int TILE_N>
+__device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int total_mt, int E,
+                                                const ProblemList& pl) {
+  const int64_t group_span = (int64_t)kGroupM * n_tiles;
+  const int64_t group = t / group_span;
+  const int64_t in_group = t - group * group_span;
+  const int64_t g0 = group * kGroupM;
+  const int gsize = (int)((total_mt - g0) < kGroupM ? (total_mt - g0) : kGroupM);
+  const int64_t nt = in_group / gsize;
+  const int gm = (int)(g0 + (in_group - nt * gsize));
+  int lo_e = 0, hi_e = E;  // largest e with mt_prefix[e] <= gm: the non-empty expert owning m-tile gm
+  while (hi_e - lo_e > 1) {
+    const int mid = (lo_e + hi_e) >> 1;
+    if (pl.mt_prefix[mid] <= gm) lo_e = mid; else hi_e = mid;
+  }
+  TileCoord c;
+  c.e = lo_e;
+  c.mi = gm - pl.mt_prefix[lo_e];
+  c.row0 = (int64_t)pl.seg_lo[lo_e] + (int64_t)c.mi * BM;
+  c.rows_valid = min(BM, pl.seg_rows[lo_e] - c.mi * BM);
+  c.n0 = nt * TILE_N;
+  return c;
+}
+
+// Registers -> bf16 tile in LDS (swizzled 16-byte chunks) -> global. For the
+// gated projection, SwiGLU is applied here: g and u are rounded to bf16 first.
+// acc[i][j][4q+s] is output row (wm*WTM + i*32 + lane%32), column
+// (block column base + 8q + 4*(lane/32) + s).
+template <int BM, int BN, bool GATED>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[Tile<BM, BN, GATED>::FM][Tile<BM, BN, GATED>::FN],
+                                         unsigned char* smem, const GemmArgs& g, const TileCoord& tc) {
+  using C = Tile<BM, BN, GATED>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  unsigned char* ot = smem;  // [BM][OUTW] bf16
+  constexpr int OUT_ROW_BYTES = C::OUTW * 2;
+  const int half_lane = lane >> 5;
+  if constexpr (GATED) {
+    constexpr int half_fn = C::FN / 2;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int r = wm * C::WTM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < half_fn; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float hv[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][4 * q + s]));
+            const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + half_fn][4 * q + s]));
+            hv[s] = gv / (1.0f + __expf(-gv)) * uv;
+          }
+          const int col = wn * (BN / 4) + j * 32 + 8 * q + 4 * half_lane;
+          const int c = col >> 3;
+          uint2 pk{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+          *reinterpret_cast<uint2*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16) + (col & 7) * 2) = pk;
+        }
+      }
     }
-    if (tid == kThreads - 1) mt_prefix[E] = scan_tmp[kThreads - 1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int r = wm * C::WTM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * C::WTN + j * 32 + 8 * q + 4 * half_lane;
+          const int c = col >> 3;
+          uint2 pk{pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
+                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          *reinterpret_cast<uint2*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16) + (col & 7) * 2) = pk;
+        }
+      }
+    }
   }
   __syncthreads();
+  constexpr int kStoreIters = BM * C::OUT_CPR / kThreads;
+#pragma unroll
+  for (int it = 0; it < kStoreIters; ++it) {
+    const int idx = it * kThreads + tid;
+    const int r = idx / C::OUT_CPR, c = idx % C::OUT_CPR;
+    const int64_t col = tc.n0 + c * 8;
+    if (r < tc.rows_valid && col < g.N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16));
+      *reinterpret_cast<u32x4*>(g.out + (tc.row0 + r) * g.ldo + col) = v;
+    }
+  }
+  __syncthreads();  // LDS is reused by the next tile
+}
 
-  const int total_mt = mt_prefix[E];
-  const int64_t n_tiles = GATED ? (N + C::OUTW - 1) / C::OUTW : (N + BN - 1) / BN;
+// weight-tile row of a wave's fn-th 32-row block
+template <int BN, bool GATED, int FN>
+__device__ __forceinline__ int b_block_row(int wn, int fn) {
+  if constexpr (GATED) {
+    constexpr int half_fn = FN / 2;
+    const int half = fn / half_fn, sub = fn % half_fn;
+    return half * (BN / 2) + wn * (BN / 4) + sub * 32;
+  } else {
+    return wn * (BN / 2) + fn * 32;
+  }
+}
+
+// ============================================================================
+// Pipelined main loop: direct global -> LDS loads into a 3-stage ring.
+// ============================================================================
+template <int BM, int BN, bool GATED, bool B_NMAJOR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_pipe_kernel(
+    GemmArgs g) {
+  using C = Tile<BM, BN, GATED>;
+  constexpr int OPS = C::A_OPS + C::B_OPS;
+  static_assert(OPS * (kStages - 1) < 64, "outstanding wave loads must fit the vmcnt counter");
+  static_assert(!B_NMAJOR || BN * 2 <= 1024, "N-major tile rows must not exceed one wave load");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ ProblemList pl;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  build_problem_list<BM>(g, pl);
+  const int total_mt = pl.mt_prefix[g.E];
+  constexpr int TILE_N = GATED ? C::OUTW : BN;
+  const int64_t n_tiles = (g.N + TILE_N - 1) / TILE_N;
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
-  const int nk = (int)((K + BK - 1) / BK);
+  const int nk = (int)(g.K / BK);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
+    const TileCoord tc = tile_coord<BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
+    const uint16_t* Wexp = g.W + (int64_t)tc.e * g.w_expert_stride;
+
+    // Source of each lane's 16-byte chunk for k0 = 0. A wave load fills 1 KB of
+    // LDS (lane l -> bytes [16l, 16l+16)), so the swizzle is applied by choosing
+    // which global chunk each lane fetches. Rows past the expert's block and
+    // columns past N are pointed at valid rows/columns: they only feed outputs
+    // that are never stored.
+    const uint16_t* a_src[C::A_OPS];
+#pragma unroll
+    for (int t2 = 0; t2 < C::A_OPS; ++t2) {
+      const int j = wave + 4 * t2;
+      const int r = 8 * j + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      const int rr = r < tc.rows_valid ? r : tc.rows_valid - 1;
+      a_src[t2] = g.A + (tc.row0 + rr) * g.lda + c * 8;
+    }
+    const uint16_t* b_src[C::B_OPS];
+#pragma unroll
+    for (int t2 = 0; t2 < C::B_OPS; ++t2) {
+      const int j = wave + 4 * t2;
+      if constexpr (!B_NMAJOR) {
+        const int r = 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        int64_t n, wrow;
+        if constexpr (GATED) {
+          const int half = r >= BN / 2 ? 1 : 0;
+          n = tc.n0 + (r - half * (BN / 2));
+          if (n >= g.N) n = tc.n0;
+          wrow = n + half * g.gate_up_rows;
+        } else {
+          n = tc.n0 + r;
+          if (n >= g.N) n = tc.n0;
+          wrow = n;
+        }
+        b_src[t2] = Wexp + wrow * g.ldw + c * 8;
+      } else {
+        // 64 k-rows of BN columns; row k keeps logical chunk c at position c ^ (2 * (k % 4)),
+        // so the 4 rows x 2 chunks that one 16-lane transpose read touches hit distinct banks.
+        constexpr int kRowsPerOp = 1024 / (BN * 2);
+        constexpr int kChunksRow = BN / 8;
+        const int r = j * kRowsPerOp + lane / kChunksRow;
+        const int c = (lane % kChunksRow) ^ (2 * (r & 3));
+        int64_t col = tc.n0 + c * 8;
+        if (col >= g.N) col = tc.n0;
+        b_src[t2] = Wexp + (int64_t)r * g.ldw + col;
+      }
+    }
+    auto issue = [&](int kt) {
+      const uint32_t sa = lds0 + (uint32_t)((kt % kStages) * C::STAGE_BYTES);
+      const uint32_t sb = sa + C::A_BYTES;
+      const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+      for (int t2 = 0; t2 < C::A_OPS; ++t2)
+        dma16(a_src[t2] + k0, __builtin_amdgcn_readfirstlane(sa + (uint32_t)((wave + 4 * t2) * 1024)));
+#pragma unroll
+      for (int t2 = 0; t2 < C::B_OPS; ++t2)
+        dma16(B_NMAJOR ? b_src[t2] + k0 * g.ldw : b_src[t2] + k0,
+              __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave + 4 * t2) * 1024)));
+    };
+
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      // Stage kt is complete for this wave once at most one later stage is in flight;
+      // after the barrier it is complete for every wave, and every wave has finished
+      // reading stage kt-1, whose slot the next issue overwrites.
+      if (kt + 1 < nk) wait_vmcnt<OPS>(); else wait_vmcnt<0>();
+      bare_barrier();
+      if (kt + 2 < nk) issue(kt + 2);
+      const unsigned char* as = smem + (kt % kStages) * C::STAGE_BYTES;
+      const unsigned char* bs = as + C::A_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int chunk = 2 * ks + (lane >> 5);
+        bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          const int r = wm * C::WTM + i * 32 + (lane & 31);
+          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + r * (BK * 2) + swz(r, chunk) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          if constexpr (!B_NMAJOR) {
+            const int r = b_block_row<BN, GATED, C::FN>(wn, j) + (lane & 31);
+            bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + r * (BK * 2) + swz(r, chunk) * 16));
+          } else {
+            // lane l gets k = 16ks + 8(l/32) + 0..7 of column nb0 + l%32: two transpose reads of
+            // 4 k each; in a 16-lane group lane j points at k-row j/4, columns 4(j%4)..+3.
+            const int nb0 = wn * C::WTN + j * 32;
+            const int c = (nb0 >> 3) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            uint2 part[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int krow = ks * 16 + 8 * (lane >> 5) + 4 * q + ((lane & 15) >> 2);
+              const unsigned char* p = bs + krow * (BN * 2) + ((c ^ (2 * (krow & 3))) * 16) + (lane & 1) * 8;
+              const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(p));
+              part[q] = __builtin_bit_cast(uint2, v);
+            }
+            bfr[j] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
+    epilogue<BM, BN, GATED>(acc, smem, g, tc);
+  }
+}
+
+// ============================================================================
+// Register-staged main loop: any K % 8 == 0 (zero fill of the K remainder).
+// ============================================================================
+template <int BM, int BN, bool GATED, bool B_NMAJOR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_regs_kernel(
+    GemmArgs g) {
+  using C = Tile<BM, BN, GATED>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ ProblemList pl;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  build_problem_list<BM>(g, pl);
+  const int total_mt = pl.mt_prefix[g.E];
+  constexpr int TILE_N = GATED ? C::OUTW : BN;
+  const int64_t n_tiles = (g.N + TILE_N - 1) / TILE_N;
+  const int64_t total_tiles = (int64_t)total_mt * n_tiles;
+  const int nk = (int)((g.K + BK - 1) / BK);
 
   unsigned char* As = smem;                   // [2][BM][BK] swizzled
   unsigned char* Bs = smem + 2 * C::A_BYTES;  // [2][BN][BK] swizzled
 
   for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
-    // ---- tile -> (expert, m-tile, n-tile); groups of kGroupM m-tiles sweep all n-tiles
-    const int64_t group_span = (int64_t)kGroupM * n_tiles;
-    const int64_t group = t / group_span;
-    const int64_t in_group = t - group * group_span;
-    const int64_t g0 = group * kGroupM;
-    const int gsize = (int)((total_mt - g0) < kGroupM ? (total_mt - g0) : kGroupM);
-    const int64_t nt = in_group / gsize;
-    const int gm = (int)(g0 + (in_group - nt * gsize));
-    int lo_e = 0, hi_e = E;  // largest e with mt_prefix[e] <= gm
-    while (hi_e - lo_e > 1) {
-      const int mid = (lo_e + hi_e) >> 1;
-      if (mt_prefix[mid] <= gm) lo_e = mid; else hi_e = mid;
-    }
-    const int e = lo_e;
-    const int mi = gm - mt_prefix[e];
-    const int64_t row0 = (int64_t)seg_lo[e] + (int64_t)mi * BM;  // first sorted row of the tile
-    const int rows_valid = min(BM, seg_rows[e] - mi * BM);
-    const uint16_t* Wexp = W + (int64_t)e * w_expert_stride;
-    const int64_t n0 = nt * (GATED ? C::OUTW : BN);  // first output column
+    const TileCoord tc = tile_coord<BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
+    const uint16_t* Wexp = g.W + (int64_t)tc.e * g.w_expert_stride;
 
-    // ---- global -> register loaders
     u32x4 ra[C::A_LOADS];
     u32x4 rb[C::B_LOADS];
     auto load_a = [&](int kt) {
@@ -168,8 +467,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int idx = i * kThreads + tid;
         const int r = idx / kChunksK, c = idx % kChunksK;
         const int64_t kk = k0 + c * 8;
-        ra[i] = (r < rows_valid && kk < K)
-                    ? *reinterpret_cast<const u32x4*>(A + (row0 + r) * lda + kk)
+        ra[i] = (r < tc.rows_valid && kk < g.K)
+                    ? *reinterpret_cast<const u32x4*>(g.A + (tc.row0 + r) * g.lda + kk)
                     : zero4();
       }
     };
@@ -183,24 +482,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           int64_t wrow, ncol;
           if constexpr (GATED) {
             const int half = r / (BN / 2);
-            ncol = n0 + (r - half * (BN / 2));
-            wrow = ncol + half * gate_up_rows;
+            ncol = tc.n0 + (r - half * (BN / 2));
+            wrow = ncol + half * g.gate_up_rows;
           } else {
-            ncol = n0 + r;
+            ncol = tc.n0 + r;
             wrow = ncol;
           }
           const int64_t kk = k0 + c * 8;
-          rb[i] = (ncol < N && kk < K) ? *reinterpret_cast<const u32x4*>(Wexp + wrow * ldw + kk) : zero4();
+          rb[i] = (ncol < g.N && kk < g.K) ? *reinterpret_cast<const u32x4*>(Wexp + wrow * g.ldw + kk) : zero4();
         }
       } else {
         // 8(k) x 8(n) block per thread: rows k0+kb*8+i, columns n0+nb*8 .. +8
         static_assert(!B_NMAJOR || C::B_LOADS == 8, "transposing loader covers the tile with one 8x8 block per thread");
         const int nb = tid % (BN / 8), kb = tid / (BN / 8);
-        const int64_t ncol = n0 + nb * 8;
+        const int64_t ncol = tc.n0 + nb * 8;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int64_t kk = k0 + kb * 8 + i;
-          rb[i] = (ncol < N && kk < K) ? *reinterpret_cast<const u32x4*>(Wexp + kk * ldw + ncol) : zero4();
+          rb[i] = (ncol < g.N && kk < g.K) ? *reinterpret_cast<const u32x4*>(Wexp + kk * g.ldw + ncol) : zero4();
         }
       }
     };
@@ -246,17 +545,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // weight-tile row of the wave's fn-th 32-row block
-    auto b_block_row = [&](int fn) {
-      if constexpr (GATED) {
-        constexpr int half_fn = C::FN / 2;
-        const int half = fn / half_fn, sub = fn % half_fn;
-        return half * (BN / 2) + wn * (BN / 4) + sub * 32;
-      } else {
-        return wn * (BN / 2) + fn * 32;
-      }
-    };
-
     load_a(0);
     load_b(0);
     store_stage(0);
@@ -281,7 +569,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-          const int r = b_block_row(j) + (lane & 31);
+          const int r = b_block_row<BN, GATED, C::FN>(wn, j) + (lane & 31);
           bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + r * (BK * 2) + swz(r, chunk) * 16));
         }
 #pragma unroll
@@ -293,87 +581,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (kt + 1 < nk) store_stage(buf ^ 1);
       __syncthreads();
     }
-
-    // ---- epilogue: registers -> bf16 tile in LDS (swizzled 16-byte chunks) -> global
-    // acc[i][j][4q+s] is output row (wm*WTM + i*32 + lane%32), column
-    // (block column base + 8q + 4*(lane/32) + s).
-    unsigned char* ot = smem;  // [BM][OUTW] bf16
-    constexpr int OUT_ROW_BYTES = C::OUTW * 2;
-    const int half_lane = lane >> 5;
-    if constexpr (GATED) {
-      constexpr int half_fn = C::FN / 2;
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int r = wm * C::WTM + i * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < half_fn; ++j) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float hv[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][4 * q + s]));
-              const float u = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + half_fn][4 * q + s]));
-              hv[s] = g / (1.0f + __expf(-g)) * u;
-            }
-            const int col = wn * (BN / 4) + j * 32 + 8 * q + 4 * half_lane;
-            const int c = col >> 3;
-            uint2 pk{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *reinterpret_cast<uint2*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16) + (col & 7) * 2) = pk;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int r = wm * C::WTM + i * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = wn * C::WTN + j * 32 + 8 * q + 4 * half_lane;
-            const int c = col >> 3;
-            uint2 pk{pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
-                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-            *reinterpret_cast<uint2*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16) + (col & 7) * 2) = pk;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int kStoreIters = BM * C::OUT_CPR / kThreads;
-#pragma unroll
-    for (int it = 0; it < kStoreIters; ++it) {
-      const int idx = it * kThreads + tid;
-      const int r = idx / C::OUT_CPR, c = idx % C::OUT_CPR;
-      const int64_t col = n0 + c * 8;
-      if (r < rows_valid && col < N) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16));
-        *reinterpret_cast<u32x4*>(out + (row0 + r) * ldo + col) = v;
-      }
-    }
-    __syncthreads();  // LDS is reused by the next tile's first stage
+    epilogue<BM, BN, GATED>(acc, smem, g, tc);
   }
 }
 
-template <int BM, int BN, bool GATED, bool B_NMAJOR>
-hipError_t launch_grouped(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t w_expert_stride, int64_t ldw,
-                          int64_t gate_up_rows, int64_t N, int64_t K, const int32_t* offsets, int E, int64_t cap_rows,
-                          uint16_t* out, int64_t ldo, hipStream_t stream) {
-  using C = Tile<BM, BN, GATED>;
-  auto kern = grouped_gemm_kernel<BM, BN, GATED, B_NMAJOR>;
-  static bool attr_set[64] = {};
+template <typename Kern>
+hipError_t launch_kernel(Kern kern, int lds_bytes, bool* attr_done, const GemmArgs& g, hipStream_t stream) {
   const int dev = current_device();
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (dev >= 0 && dev < 64 && !attr_done[dev]) {
+    hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        lds_bytes);
     if (st != hipSuccess) return st;
-    attr_set[dev] = true;
+    attr_done[dev] = true;
   }
-  const int grid = device_cu_count(dev);  // one 128 KB-LDS workgroup per CU
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), C::LDS_BYTES, stream, A, lda, W, w_expert_stride, ldw,
-                     gate_up_rows, N, K, offsets, E, cap_rows, out, ldo);
+  const int grid = device_cu_count(dev);  // one workgroup per CU (the LDS ring fills it)
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes, stream, g);
   return hipGetLastError();
+}
+
+template <int BM, int BN, bool GATED, bool B_NMAJOR>
+hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
+  using C = Tile<BM, BN, GATED>;
+  if (g.K % BK == 0) {
+    static bool done[64] = {};
+    return launch_kernel(grouped_gemm_pipe_kernel<BM, BN, GATED, B_NMAJOR>, kStages * C::STAGE_BYTES, done, g, stream);
+  }
+  static bool done[64] = {};
+  return launch_kernel(grouped_gemm_regs_kernel<BM, BN, GATED, B_NMAJOR>, 2 * C::STAGE_BYTES, done, g, stream);
 }
 
 }  // namespace
@@ -382,15 +616,15 @@ hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets,
                                  int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
                                  hipStream_t stream) {
   // A = x_perm [cap, d] (K = d); weights [E, 2h, d], gate rows n, up rows h + n; out h_buf [cap, h]
-  return launch_grouped<128, 256, true, false>(x_perm, d, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h,
-                                               stream);
+  const GemmArgs g{x_perm, d, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h};
+  return launch_grouped<128, 256, true, false>(g, stream);
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down, int64_t cap_rows,
                             int64_t d, int64_t h, int32_t E, uint16_t* y_perm, hipStream_t stream) {
   // A = h_buf [cap, h] (K = h); weights [E, h, d] N-contiguous; out y_perm [cap, d]
-  return launch_grouped<128, 256, false, true>(h_buf, h, w_down, h * d, d, 0, d, h, offsets, E, cap_rows, y_perm, d,
-                                               stream);
+  const GemmArgs g{h_buf, h, w_down, h * d, d, 0, d, h, offsets, E, cap_rows, y_perm, d};
+  return launch_grouped<128, 256, false, true>(g, stream);
 }
 
 }  // namespace moe
