@@ -200,7 +200,7 @@ def main(argv=None):
                                 steps=max(3, min(args.steps, 10)))
 
     if args.calib_copy:
-        src = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
+        src = torch.full((256 << 20,), 7, dtype=torch.uint8, device=dev)  # written first: a real read stream
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)

@@ -40,7 +40,6 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves
 constexpr int BK = 64;         // K per stage: 8 chunks of 16 bytes per tile row
 constexpr int kChunksK = BK / 8;
 constexpr int kGroupM = 8;     // m-tiles per group in the tile order (operand reuse in L2)
@@ -49,22 +48,28 @@ constexpr int kStages = 3;     // LDS ring depth of the pipelined loop
 #define LDS_AS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-template <int BM, int BN, bool GATED>
+// Tile geometry: BM x BN weight rows per workgroup, WGM x WGN waves, NST LDS stages.
+template <int BM_, int BN_, int WGM_, int WGN_, int NST_, bool GATED_>
 struct Tile {
-  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, NST = NST_;
+  static constexpr bool GATED = GATED_;
+  static constexpr int NWAVES = WGM * WGN, THREADS = 64 * NWAVES;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int OUTW = GATED ? BN / 2 : BN;  // output columns per tile
   static constexpr int OUT_CPR = OUTW / 8;          // 16-byte chunks per output row
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int A_LOADS = BM * kChunksK / kThreads;  // register path: 16-byte chunks per thread
-  static constexpr int B_LOADS = BN * kChunksK / kThreads;
-  static constexpr int A_OPS = A_BYTES / 1024 / 4;  // pipelined path: 1 KB wave loads per wave per stage
-  static constexpr int B_OPS = B_BYTES / 1024 / 4;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 32x32 blocks over a 2x2 wave grid");
-  static_assert(BM * OUTW * 2 <= 2 * STAGE_BYTES, "epilogue tile must fit in the stage buffers");
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static constexpr int A_LOADS = BM * kChunksK / THREADS;  // register path: 16-byte chunks per thread
+  static constexpr int B_LOADS = BN * kChunksK / THREADS;
+  static constexpr int A_OPS = A_BYTES / 1024 / NWAVES;  // pipelined path: 1 KB wave loads per wave per stage
+  static constexpr int B_OPS = B_BYTES / 1024 / NWAVES;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must split into 32x32 blocks");
+  static_assert(BM * OUTW * 2 <= LDS_BYTES, "epilogue tile must fit in the stage buffers");
   static_assert((OUT_CPR & (OUT_CPR - 1)) == 0, "output chunk count must be a power of two");
   static_assert(!GATED || FN % 2 == 0, "gated tiles pair gate and up blocks");
+  static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0, "stage must split into wave loads");
 };
 
 struct GemmArgs {
@@ -83,11 +88,12 @@ struct GemmArgs {
   int64_t ldo;
 };
 
+template <int THREADS>
 struct ProblemList {
   int seg_lo[MOE_MAX_EXPERTS];
   int seg_rows[MOE_MAX_EXPERTS];
   int mt_prefix[MOE_MAX_EXPERTS + 1];
-  int scan_tmp[kThreads];
+  int scan_tmp[THREADS];
 };
 
 struct TileCoord {
@@ -98,7 +104,16 @@ struct TileCoord {
   int64_t n0;       // first output column
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// K-contiguous tile rows are 128 B (8 chunks of 16 B). LDS has 64 banks (256 B
+// per cycle), so two rows share a bank window and a 16-lane read group spans 16
+// rows: chunk c of row r is kept at position c ^ ((r / 2) % 8), which gives the
+// 16 rows of a group 16 distinct (window half, position) pairs.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// N-contiguous rows (W_down tiles) are BN*2 bytes. A 32-lane half of a transpose
+// read touches 4 rows x 4 consecutive chunks; chunk c of row k is kept at
+// c ^ (4 * (k % 4)), which spreads those 16 chunks over the 16 bank positions.
+__device__ __forceinline__ int swz_n(int krow, int chunk) { return chunk ^ (4 * (krow & 3)); }
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
@@ -133,10 +148,10 @@ __device__ __forceinline__ int logical_worker() {
 
 // Problem list from the device offsets, clamped so no access leaves the buffers:
 // per expert its first row, its row count and the prefix of its m-tile counts.
-template <int BM>
-__device__ void build_problem_list(const GemmArgs& g, ProblemList& pl) {
+template <int BM, int THREADS>
+__device__ void build_problem_list(const GemmArgs& g, ProblemList<THREADS>& pl) {
   const int tid = threadIdx.x;
-  constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
+  constexpr int kPer = (MOE_MAX_EXPERTS + THREADS - 1) / THREADS;
   int mt_local[kPer];
   int sum = 0;
 #pragma unroll
@@ -156,7 +171,7 @@ __device__ void build_problem_list(const GemmArgs& g, ProblemList& pl) {
   }
   pl.scan_tmp[tid] = sum;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
+  for (int off = 1; off < THREADS; off <<= 1) {
     const int add = tid >= off ? pl.scan_tmp[tid - off] : 0;
     __syncthreads();
     pl.scan_tmp[tid] += add;
@@ -169,16 +184,16 @@ __device__ void build_problem_list(const GemmArgs& g, ProblemList& pl) {
     if (e < g.E) pl.mt_prefix[e] = run;
     run += mt_local[i];
   }
-  if (tid == kThreads - 1) pl.mt_prefix[g.E] = pl.scan_tmp[kThreads - 1];
+  if (tid == THREADS - 1) pl.mt_prefix[g.E] = pl.scan_tmp[THREADS - 1];
   __syncthreads();
 }
 
 // Tile t -> (expert, m-tile, n-tile). Groups of kGroupM consecutive m-tiles
 // sweep every n-tile before the next group starts, so tiles that run at the
 // same time share A rows and weight rows.
-template <int BM, int TILE_N>
+template <int BM, int TILE_N, int THREADS>
 __device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int total_mt, int E,
-                                                const ProblemList& pl) {
+                                                const ProblemList<THREADS>& pl) {
   const int64_t group_span = (int64_t)kGroupM * n_tiles;
   const int64_t group = t / group_span;
   const int64_t in_group = t - group * group_span;
@@ -204,16 +219,16 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int 
 // gated projection, SwiGLU is applied here: g and u are rounded to bf16 first.
 // acc[i][j][4q+s] is output row (wm*WTM + i*32 + lane%32), column
 // (block column base + 8q + 4*(lane/32) + s).
-template <int BM, int BN, bool GATED>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[Tile<BM, BN, GATED>::FM][Tile<BM, BN, GATED>::FN],
-                                         unsigned char* smem, const GemmArgs& g, const TileCoord& tc) {
-  using C = Tile<BM, BN, GATED>;
+template <class C>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsigned char* smem, const GemmArgs& g,
+                                         const TileCoord& tc) {
+  constexpr int BM = C::BM, BN = C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   unsigned char* ot = smem;  // [BM][OUTW] bf16
   constexpr int OUT_ROW_BYTES = C::OUTW * 2;
   const int half_lane = lane >> 5;
-  if constexpr (GATED) {
+  if constexpr (C::GATED) {
     constexpr int half_fn = C::FN / 2;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
@@ -229,7 +244,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[Tile<BM, BN, GATED>
             const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + half_fn][4 * q + s]));
             hv[s] = gv / (1.0f + __expf(-gv)) * uv;
           }
-          const int col = wn * (BN / 4) + j * 32 + 8 * q + 4 * half_lane;
+          const int col = wn * (BN / 2 / C::WGN) + j * 32 + 8 * q + 4 * half_lane;
           const int c = col >> 3;
           uint2 pk{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
           *reinterpret_cast<uint2*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16) + (col & 7) * 2) = pk;
@@ -254,10 +269,10 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[Tile<BM, BN, GATED>
     }
   }
   __syncthreads();
-  constexpr int kStoreIters = BM * C::OUT_CPR / kThreads;
+  constexpr int kStoreIters = BM * C::OUT_CPR / C::THREADS;
 #pragma unroll
   for (int it = 0; it < kStoreIters; ++it) {
-    const int idx = it * kThreads + tid;
+    const int idx = it * C::THREADS + tid;
     const int r = idx / C::OUT_CPR, c = idx % C::OUT_CPR;
     const int64_t col = tc.n0 + c * 8;
     if (r < tc.rows_valid && col < g.N) {
@@ -268,46 +283,47 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[Tile<BM, BN, GATED>
   __syncthreads();  // LDS is reused by the next tile
 }
 
-// weight-tile row of a wave's fn-th 32-row block
-template <int BN, bool GATED, int FN>
+// weight-tile row of a wave's fn-th 32-row block (gated: the first FN/2 blocks are gate rows,
+// the rest the matching up rows, BN/2 further down)
+template <class C>
 __device__ __forceinline__ int b_block_row(int wn, int fn) {
-  if constexpr (GATED) {
-    constexpr int half_fn = FN / 2;
+  if constexpr (C::GATED) {
+    constexpr int half_fn = C::FN / 2;
     const int half = fn / half_fn, sub = fn % half_fn;
-    return half * (BN / 2) + wn * (BN / 4) + sub * 32;
+    return half * (C::BN / 2) + wn * (C::BN / 2 / C::WGN) + sub * 32;
   } else {
-    return wn * (BN / 2) + fn * 32;
+    return wn * C::WTN + fn * 32;
   }
 }
 
 // ============================================================================
-// Pipelined main loop: direct global -> LDS loads into a 3-stage ring.
+// Pipelined main loop: direct global -> LDS loads into an NST-stage ring.
 // ============================================================================
-template <int BM, int BN, bool GATED, bool B_NMAJOR>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_pipe_kernel(
-    GemmArgs g) {
-  using C = Tile<BM, BN, GATED>;
+template <class C, bool B_NMAJOR>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs g) {
+  constexpr int BN = C::BN, NST = C::NST;
   constexpr int OPS = C::A_OPS + C::B_OPS;
-  static_assert(OPS * (kStages - 1) < 64, "outstanding wave loads must fit the vmcnt counter");
+  static_assert(OPS * (NST - 1) < 64, "outstanding wave loads must fit the vmcnt counter");
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(!B_NMAJOR || BN * 2 <= 1024, "N-major tile rows must not exceed one wave load");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ ProblemList pl;
+  __shared__ ProblemList<C::THREADS> pl;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-  build_problem_list<BM>(g, pl);
+  build_problem_list<C::BM>(g, pl);
   const int total_mt = pl.mt_prefix[g.E];
-  constexpr int TILE_N = GATED ? C::OUTW : BN;
+  constexpr int TILE_N = C::GATED ? C::OUTW : BN;
   const int64_t n_tiles = (g.N + TILE_N - 1) / TILE_N;
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
   const int nk = (int)(g.K / BK);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
-    const TileCoord tc = tile_coord<BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
+    const TileCoord tc = tile_coord<C::BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
     const uint16_t* Wexp = g.W + (int64_t)tc.e * g.w_expert_stride;
 
     // Source of each lane's 16-byte chunk for k0 = 0. A wave load fills 1 KB of
@@ -318,21 +334,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint16_t* a_src[C::A_OPS];
 #pragma unroll
     for (int t2 = 0; t2 < C::A_OPS; ++t2) {
-      const int j = wave + 4 * t2;
+      const int j = wave + C::NWAVES * t2;
       const int r = 8 * j + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
+      const int c = swz(r, lane & 7);  // the swizzle is an involution: position -> logical chunk
       const int rr = r < tc.rows_valid ? r : tc.rows_valid - 1;
       a_src[t2] = g.A + (tc.row0 + rr) * g.lda + c * 8;
     }
     const uint16_t* b_src[C::B_OPS];
 #pragma unroll
     for (int t2 = 0; t2 < C::B_OPS; ++t2) {
-      const int j = wave + 4 * t2;
+      const int j = wave + C::NWAVES * t2;
       if constexpr (!B_NMAJOR) {
         const int r = 8 * j + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
+        const int c = swz(r, lane & 7);
         int64_t n, wrow;
-        if constexpr (GATED) {
+        if constexpr (C::GATED) {
           const int half = r >= BN / 2 ? 1 : 0;
           n = tc.n0 + (r - half * (BN / 2));
           if (n >= g.N) n = tc.n0;
@@ -344,28 +360,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
         b_src[t2] = Wexp + wrow * g.ldw + c * 8;
       } else {
-        // 64 k-rows of BN columns; row k keeps logical chunk c at position c ^ (2 * (k % 4)),
-        // so the 4 rows x 2 chunks that one 16-lane transpose read touches hit distinct banks.
+        // 64 k-rows of BN columns, chunk positions swizzled by swz_n
         constexpr int kRowsPerOp = 1024 / (BN * 2);
         constexpr int kChunksRow = BN / 8;
         const int r = j * kRowsPerOp + lane / kChunksRow;
-        const int c = (lane % kChunksRow) ^ (2 * (r & 3));
+        const int c = swz_n(r, lane % kChunksRow);
         int64_t col = tc.n0 + c * 8;
         if (col >= g.N) col = tc.n0;
         b_src[t2] = Wexp + (int64_t)r * g.ldw + col;
       }
     }
     auto issue = [&](int kt) {
-      const uint32_t sa = lds0 + (uint32_t)((kt % kStages) * C::STAGE_BYTES);
+      const uint32_t sa = lds0 + (uint32_t)((kt % NST) * C::STAGE_BYTES);
       const uint32_t sb = sa + C::A_BYTES;
       const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
       for (int t2 = 0; t2 < C::A_OPS; ++t2)
-        dma16(a_src[t2] + k0, __builtin_amdgcn_readfirstlane(sa + (uint32_t)((wave + 4 * t2) * 1024)));
+        dma16(a_src[t2] + k0, __builtin_amdgcn_readfirstlane(sa + (uint32_t)((wave + C::NWAVES * t2) * 1024)));
 #pragma unroll
       for (int t2 = 0; t2 < C::B_OPS; ++t2)
         dma16(B_NMAJOR ? b_src[t2] + k0 * g.ldw : b_src[t2] + k0,
-              __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave + 4 * t2) * 1024)));
+              __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave + C::NWAVES * t2) * 1024)));
     };
 
     f32x16 acc[C::FM][C::FN];
@@ -376,16 +391,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    issue(0);
-    if (nk > 1) issue(1);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nk) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
-      // Stage kt is complete for this wave once at most one later stage is in flight;
-      // after the barrier it is complete for every wave, and every wave has finished
-      // reading stage kt-1, whose slot the next issue overwrites.
-      if (kt + 1 < nk) wait_vmcnt<OPS>(); else wait_vmcnt<0>();
+      // Stage kt is complete for this wave once only the later stages already issued are
+      // in flight; after the barrier it is complete for every wave, and every wave has
+      // finished reading stage kt-1, whose slot the next issue overwrites.
+      const int ahead = min(nk, kt + NST - 1) - kt - 1;
+      if (NST >= 4 && ahead >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * OPS>();
+      else if (NST >= 3 && ahead >= 1) wait_vmcnt<(NST >= 3 ? 1 : 0) * OPS>();
+      else wait_vmcnt<0>();
       bare_barrier();
-      if (kt + 2 < nk) issue(kt + 2);
-      const unsigned char* as = smem + (kt % kStages) * C::STAGE_BYTES;
+      if (kt + NST - 1 < nk) issue(kt + NST - 1);
+      const unsigned char* as = smem + (kt % NST) * C::STAGE_BYTES;
       const unsigned char* bs = as + C::A_BYTES;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
@@ -399,7 +418,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
           if constexpr (!B_NMAJOR) {
-            const int r = b_block_row<BN, GATED, C::FN>(wn, j) + (lane & 31);
+            const int r = b_block_row<C>(wn, j) + (lane & 31);
             bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + r * (BK * 2) + swz(r, chunk) * 16));
           } else {
             // lane l gets k = 16ks + 8(l/32) + 0..7 of column nb0 + l%32: two transpose reads of
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const int krow = ks * 16 + 8 * (lane >> 5) + 4 * q + ((lane & 15) >> 2);
-              const unsigned char* p = bs + krow * (BN * 2) + ((c ^ (2 * (krow & 3))) * 16) + (lane & 1) * 8;
+              const unsigned char* p = bs + krow * (BN * 2) + swz_n(krow, c) * 16 + (lane & 1) * 8;
               const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(p));
               part[q] = __builtin_bit_cast(uint2, v);
             }
@@ -425,28 +444,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
     __syncthreads();  // every wave is done with the ring before the epilogue reuses it
-    epilogue<BM, BN, GATED>(acc, smem, g, tc);
+    epilogue<C>(acc, smem, g, tc);
   }
 }
 
 // ============================================================================
 // Register-staged main loop: any K % 8 == 0 (zero fill of the K remainder).
 // ============================================================================
-template <int BM, int BN, bool GATED, bool B_NMAJOR>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_regs_kernel(
-    GemmArgs g) {
-  using C = Tile<BM, BN, GATED>;
+template <class C, bool B_NMAJOR>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs g) {
+  constexpr int BN = C::BN;
+  static_assert(C::NST == 2, "register-staged loop double-buffers");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ ProblemList pl;
+  __shared__ ProblemList<C::THREADS> pl;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-  build_problem_list<BM>(g, pl);
+  build_problem_list<C::BM>(g, pl);
   const int total_mt = pl.mt_prefix[g.E];
-  constexpr int TILE_N = GATED ? C::OUTW : BN;
+  constexpr int TILE_N = C::GATED ? C::OUTW : BN;
   const int64_t n_tiles = (g.N + TILE_N - 1) / TILE_N;
   const int64_t total_tiles = (int64_t)total_mt * n_tiles;
   const int nk = (int)((g.K + BK - 1) / BK);
@@ -455,7 +474,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   unsigned char* Bs = smem + 2 * C::A_BYTES;  // [2][BN][BK] swizzled
 
   for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
-    const TileCoord tc = tile_coord<BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
+    const TileCoord tc = tile_coord<C::BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
     const uint16_t* Wexp = g.W + (int64_t)tc.e * g.w_expert_stride;
 
     u32x4 ra[C::A_LOADS];
@@ -464,7 +483,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
-        const int idx = i * kThreads + tid;
+        const int idx = i * C::THREADS + tid;
         const int r = idx / kChunksK, c = idx % kChunksK;
         const int64_t kk = k0 + c * 8;
         ra[i] = (r < tc.rows_valid && kk < g.K)
@@ -477,10 +496,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if constexpr (!B_NMAJOR) {
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
-          const int idx = i * kThreads + tid;
+          const int idx = i * C::THREADS + tid;
           const int r = idx / kChunksK, c = idx % kChunksK;
           int64_t wrow, ncol;
-          if constexpr (GATED) {
+          if constexpr (C::GATED) {
             const int half = r / (BN / 2);
             ncol = tc.n0 + (r - half * (BN / 2));
             wrow = ncol + half * g.gate_up_rows;
@@ -493,7 +512,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
       } else {
         // 8(k) x 8(n) block per thread: rows k0+kb*8+i, columns n0+nb*8 .. +8
-        static_assert(!B_NMAJOR || C::B_LOADS == 8, "transposing loader covers the tile with one 8x8 block per thread");
+        static_assert(!B_NMAJOR || (C::B_LOADS == 8 && (BK / 8) * (BN / 8) == C::THREADS),
+                      "transposing loader covers the tile with one 8x8 block per thread");
         const int nb = tid % (BN / 8), kb = tid / (BN / 8);
         const int64_t ncol = tc.n0 + nb * 8;
 #pragma unroll
@@ -508,14 +528,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       unsigned char* bs = Bs + buf * C::B_BYTES;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
-        const int idx = i * kThreads + tid;
+        const int idx = i * C::THREADS + tid;
         const int r = idx / kChunksK, c = idx % kChunksK;
         *reinterpret_cast<u32x4*>(as + r * (BK * 2) + swz(r, c) * 16) = ra[i];
       }
       if constexpr (!B_NMAJOR) {
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
-          const int idx = i * kThreads + tid;
+          const int idx = i * C::THREADS + tid;
           const int r = idx / kChunksK, c = idx % kChunksK;
           *reinterpret_cast<u32x4*>(bs + r * (BK * 2) + swz(r, c) * 16) = rb[i];
         }
@@ -569,7 +589,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
-          const int r = b_block_row<BN, GATED, C::FN>(wn, j) + (lane & 31);
+          const int r = b_block_row<C>(wn, j) + (lane & 31);
           bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + r * (BK * 2) + swz(r, chunk) * 16));
         }
 #pragma unroll
@@ -581,33 +601,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (kt + 1 < nk) store_stage(buf ^ 1);
       __syncthreads();
     }
-    epilogue<BM, BN, GATED>(acc, smem, g, tc);
+    epilogue<C>(acc, smem, g, tc);
   }
 }
 
-template <typename Kern>
-hipError_t launch_kernel(Kern kern, int lds_bytes, bool* attr_done, const GemmArgs& g, hipStream_t stream) {
+template <class C, typename Kern>
+hipError_t launch_kernel(Kern kern, bool* attr_done, const GemmArgs& g, hipStream_t stream) {
   const int dev = current_device();
   if (dev >= 0 && dev < 64 && !attr_done[dev]) {
     hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        lds_bytes);
+                                        C::LDS_BYTES);
     if (st != hipSuccess) return st;
     attr_done[dev] = true;
   }
-  const int grid = device_cu_count(dev);  // one workgroup per CU (the LDS ring fills it)
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes, stream, g);
+  const int grid = device_cu_count(dev);  // one workgroup per CU: the LDS ring fills it
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, g);
   return hipGetLastError();
 }
 
-template <int BM, int BN, bool GATED, bool B_NMAJOR>
+// Tile configurations. Large expert blocks (mean rows per expert >= 384) take
+// 256 x 256 tiles on 8 waves (two per SIMD, so one wave's LDS and barrier waits
+// overlap the other's MFMAs) with a 2-stage ring; smaller blocks take 128 x 256
+// tiles on 4 waves with a 3-stage ring, which wastes fewer rows on ragged
+// tails. K not a multiple of 64 takes the register-staged loop.
+template <bool GATED>
+using BigTile = Tile<256, 256, 2, 4, 2, GATED>;
+template <bool GATED>
+using SmallTile = Tile<128, 256, 2, 2, 3, GATED>;
+template <bool GATED>
+using RegsTile = Tile<128, 256, 2, 2, 2, GATED>;
+
+template <bool GATED, bool B_NMAJOR>
 hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
-  using C = Tile<BM, BN, GATED>;
   if (g.K % BK == 0) {
+    if (g.cap_rows >= (int64_t)384 * g.E) {
+      static bool done[64] = {};
+      return launch_kernel<BigTile<GATED>>(grouped_gemm_pipe_kernel<BigTile<GATED>, B_NMAJOR>, done, g, stream);
+    }
     static bool done[64] = {};
-    return launch_kernel(grouped_gemm_pipe_kernel<BM, BN, GATED, B_NMAJOR>, kStages * C::STAGE_BYTES, done, g, stream);
+    return launch_kernel<SmallTile<GATED>>(grouped_gemm_pipe_kernel<SmallTile<GATED>, B_NMAJOR>, done, g, stream);
   }
   static bool done[64] = {};
-  return launch_kernel(grouped_gemm_regs_kernel<BM, BN, GATED, B_NMAJOR>, 2 * C::STAGE_BYTES, done, g, stream);
+  return launch_kernel<RegsTile<GATED>>(grouped_gemm_regs_kernel<RegsTile<GATED>, B_NMAJOR>, done, g, stream);
 }
 
 }  // namespace
@@ -617,14 +652,14 @@ hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets,
                                  hipStream_t stream) {
   // A = x_perm [cap, d] (K = d); weights [E, 2h, d], gate rows n, up rows h + n; out h_buf [cap, h]
   const GemmArgs g{x_perm, d, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h};
-  return launch_grouped<128, 256, true, false>(g, stream);
+  return launch_grouped<true, false>(g, stream);
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down, int64_t cap_rows,
                             int64_t d, int64_t h, int32_t E, uint16_t* y_perm, hipStream_t stream) {
   // A = h_buf [cap, h] (K = h); weights [E, h, d] N-contiguous; out y_perm [cap, d]
   const GemmArgs g{h_buf, h, w_down, h * d, d, 0, d, h, offsets, E, cap_rows, y_perm, d};
-  return launch_grouped<128, 256, false, true>(g, stream);
+  return launch_grouped<false, true>(g, stream);
 }
 
 }  // namespace moe

@@ -80,6 +80,11 @@ def _fuzz_cases():
         dict(T=64, k=4, E=1, d=8, h=8, seed=4, drop_frac=0.0),
         dict(T=40, k=2, E=1024, d=64, h=64, seed=5, drop_frac=0.1),
         dict(T=33, k=2, E=6, d=64, h=64, seed=6, drop_frac=1.0),  # every slot dropped: M = 0
+        # K % 64 == 0 with N and M tails: large blocks (>= 384 rows per expert) take the 256 x 256
+        # tile, smaller ones the 128 x 256 tile
+        dict(T=900, k=2, E=3, d=320, h=192, seed=7, drop_frac=0.05),
+        dict(T=200, k=3, E=4, d=320, h=192, seed=8, drop_frac=0.05, empty_experts=(2,)),
+        dict(T=1100, k=1, E=2, d=576, h=448, seed=9, drop_frac=0.0),
     ]
     return cases
 
