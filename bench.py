@@ -92,7 +92,7 @@ def main(argv=None):
     ap.add_argument("--config", default="zipf64", choices=["toy", "edge", "qwen3_30b", "zipf64", "square"])
     ap.add_argument("--no-variants", action="store_true", help="skip the padded-BMM and per-expert-loop variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0: a quarter of T)")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0: all T tokens)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -208,7 +208,7 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu_baseline:
-        tokens = args.cpu_tokens or max(1, T // 4)
+        tokens = args.cpu_tokens or T
         cpu = cpu_baseline(wl, min(tokens, T))
 
     out = {
