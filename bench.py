@@ -45,11 +45,15 @@ def useful_flops(M: int, d: int, h: int) -> int:
     return 6 * M * d * h
 
 
-def algorithmic_bytes(T, k, M, d, h, nonempty):
-    """Bytes each stage must move at minimum (bf16 = 2 B, int32/fp32 = 4 B); see the design doc."""
+def algorithmic_bytes(T, k, M, d, h, nonempty, fused=True):
+    """Bytes each stage must move at minimum (bf16 = 2 B, int32/fp32 = 4 B); see the design doc.
+
+    fused: the permute writes index maps only and the gate/up GEMM reads each token row of X once at minimum;
+    otherwise the permute also copies rows into x_perm, which the GEMM reads back.
+    """
     S = T * k
-    permute = 2 * T * d + 2 * M * d + 4 * S * 3  # read X once, write x_perm, ids + perm + inv
-    gemm1 = 2 * M * d + nonempty * 2 * (2 * h) * d + 2 * M * h
+    permute = 4 * S * 3 + (0 if fused else 2 * T * d + 2 * M * d)  # ids + perm + inv (+ read X, write x_perm)
+    gemm1 = (2 * T * d if fused else 2 * M * d) + nonempty * 2 * (2 * h) * d + 2 * M * h
     gemm2 = 2 * M * h + nonempty * 2 * h * d + 2 * M * d
     unpermute = 2 * M * d + 8 * S + 2 * T * d
     return {"permute": permute, "gemm_up_swiglu": gemm1, "gemm_down": gemm2, "unpermute": unpermute}
@@ -93,6 +97,8 @@ def main(argv=None):
     ap.add_argument("--no-variants", action="store_true", help="skip the padded-BMM and per-expert-loop variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0: all T tokens)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="copy rows into x_perm in moe_permute instead of gathering them inside the gate/up GEMM")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -107,7 +113,7 @@ def main(argv=None):
     import torch
 
     import ragged_grouped_gemm_histogram_amd as moe
-    from workloads import make_workload
+    from workloads import WORKLOADS, make_workload
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -123,7 +129,8 @@ def main(argv=None):
     x, w_ug, w_down = bf(wl.x), bf(wl.w_ug), bf(wl.w_down)
     ids = torch.from_numpy(wl.expert_ids).to(dev)
     rw = torch.from_numpy(wl.routing_w).to(dev)
-    x_perm = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+    fused = not args.unfused
+    x_perm = None if fused else torch.empty((S, d), dtype=torch.bfloat16, device=dev)
     h_buf = torch.empty((S, h), dtype=torch.bfloat16, device=dev)
     y_perm = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
@@ -137,10 +144,13 @@ def main(argv=None):
         if ev is not None:
             ev[0].record()
         p = moe.moe_permute(x, ids, E, x_perm=x_perm, counts=counts, offsets=offsets, perm=perm, inv_map=inv,
-                            workspace=ws)
+                            workspace=ws, gather=not fused)
         if ev is not None:
             ev[1].record()
-        moe.moe_gemm_up_swiglu(p.x_perm, p.offsets, w_ug, h_buf=h_buf)
+        if fused:
+            moe.moe_gemm_up_swiglu_gather(x, p.perm, p.offsets, w_ug, k, h_buf=h_buf)
+        else:
+            moe.moe_gemm_up_swiglu(p.x_perm, p.offsets, w_ug, h_buf=h_buf)
         if ev is not None:
             ev[2].record()
         moe.moe_gemm_down(h_buf, p.offsets, w_down, y_perm=y_perm)
@@ -169,7 +179,7 @@ def main(argv=None):
     value = flops / (ms_per_step * 1e-3) / 1e12
     names = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
     stage_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
-    algo = algorithmic_bytes(T, k, M, d, h, nonempty)
+    algo = algorithmic_bytes(T, k, M, d, h, nonempty, fused)
     gemm1_flops = 2 * M * d * (2 * h)
     gemm2_flops = 2 * M * h * d
     stages = {
@@ -187,16 +197,19 @@ def main(argv=None):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("gemm_src_sha") == file_sha(GEMM_SRC) and tr.get("workload") == wl.name:
+        if (tr.get("gemm_src_sha") == file_sha(GEMM_SRC) and tr.get("workload") == wl.name
+                and tr.get("fused_gather", False) == fused):
             traffic = tr.get("bytes_per_launch")
-    roofline = {"bound": "mfma", "kernel": "grouped_gemm_kernel<gate/up + SwiGLU>", "achieved": achieved,
+    roofline = {"bound": "mfma", "kernel": "grouped_gemm_pipe_kernel<gate/up + SwiGLU" + (", fused gather>" if fused else ">"),
+                "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic, "algorithmic_bytes": algo["gemm_up_swiglu"], "flops_per_launch": gemm1_flops,
                 "avg_launch_ms": g1_ms}
 
     variants = None
     if not args.no_variants:
-        variants = run_variants(torch, moe, x, ids, rw, w_ug, w_down, wl, counts, offsets, x_perm, inv, y_perm, ws,
+        xp = x_perm if x_perm is not None else torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+        variants = run_variants(torch, moe, x, ids, rw, w_ug, w_down, wl, counts, offsets, xp, inv, y_perm, ws,
                                 steps=max(3, min(args.steps, 10)))
 
     if args.calib_copy:
@@ -225,7 +238,8 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "k": k, "E": E, "d": d, "h": h, "M": M, "nonempty_experts": nonempty,
-                   "seed": 4 if wl.name == "zipf64" else None, "parallelism": "single GPU"},
+                   "seed": WORKLOADS[wl.name][0], "parallelism": "single GPU",
+                   "gather": "fused into the gate/up GEMM" if fused else "x_perm copy in moe_permute"},
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "useful_gflop": flops / 1e9,
         "stages": stages,

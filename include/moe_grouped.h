@@ -77,7 +77,10 @@ size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
  *   expert_ids  int32 [T, k]  routed expert of each slot; any id outside
  *                             [0, E) (such as the -1 padding of an expert-
  *                             parallel dispatch) marks a dropped slot
- *   x_perm      bf16  [T*k, d] out: rows [0, M) hold X[perm[p] / k]
+ *   x_perm      bf16  [T*k, d] out: rows [0, M) hold X[perm[p] / k]; may be NULL,
+ *                             then no rows are copied (x is then not read and
+ *                             may be NULL too) and a *_gather GEMM call reads
+ *                             X through perm instead
  *   counts      int32 [E]     out: kept slots per expert
  *   offsets     int32 [E+1]   out: offsets[0] = 0, offsets[e+1] =
  *                             offsets[e] + counts[e]; expert e owns sorted
@@ -103,10 +106,10 @@ moe_status moe_permute(const uint16_t* x, const int32_t* expert_ids, int64_t T, 
  *   Y_e = bf16( H_e * W_down[e] )                    written to y_perm[rows]
  *
  *   x_perm   bf16  [cap_rows, d]
- *   offsets  int32 [E+1]       device offsets as written by moe_permute; they
- *                              are clamped to [0, cap_rows] and made monotone
- *                              on the device, so no row outside the buffers is
- *                              ever touched
+ *   offsets  int32 [E+1]       device offsets as written by moe_permute; each is
+ *                              clamped into [0, cap_rows] on the device (an
+ *                              expert whose end precedes its start is empty),
+ *                              so no row outside the buffers is ever touched
  *   w_ug     bf16  [E, 2h, d]  gate rows [0, h), up rows [h, 2h)
  *   w_down   bf16  [E, h, d]
  *   h_buf    bf16  [cap_rows, h] out (the SwiGLU activations)
@@ -125,6 +128,31 @@ moe_status grouped_swiglu_expert(const uint16_t* x_perm, const int32_t* offsets,
 moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
                               int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
                               hipStream_t stream);
+
+/* The first half with the permuted gather fused into its loads (OLMo report
+ * Sec 9.4: the up/gate projection reads the dispatch buffer directly instead
+ * of a permuted copy). Sorted row p of expert e's block reads token row
+ * x[perm[p] / k]; nothing else changes:
+ *
+ *   x        bf16  [T, d]    token rows
+ *   perm     int32 [T*k]     as written by moe_permute (entries [0, M) are read;
+ *                            out-of-range entries are clamped, never faulting)
+ *   offsets  int32 [E+1]     as written by moe_permute
+ *   w_ug     bf16  [E, 2h, d]
+ *   h_buf    bf16  [T*k, h]  out
+ *
+ * One kernel launch; same results as moe_permute's x_perm followed by
+ * moe_gemm_up_swiglu, bit for bit. */
+moe_status moe_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
+                                     const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
+                                     uint16_t* h_buf, hipStream_t stream);
+
+/* moe_gemm_up_swiglu_gather followed by moe_gemm_down (cap_rows = T*k): the
+ * grouped SwiGLU expert on token rows gathered through perm. */
+moe_status grouped_swiglu_expert_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
+                                        const int32_t* offsets, const uint16_t* w_ug, const uint16_t* w_down,
+                                        int64_t d, int64_t h, int32_t E, uint16_t* h_buf, uint16_t* y_perm,
+                                        hipStream_t stream);
 
 /* The second half alone: one kernel launch that writes y_perm[rows] =
  * bf16(h_buf[rows] * W_down[e]). Arguments as above. */

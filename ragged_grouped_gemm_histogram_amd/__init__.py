@@ -32,6 +32,9 @@ _SIGNATURES = {
     "grouped_swiglu_expert": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_gemm_up_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "moe_gemm_down": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_gemm_up_swiglu_gather": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "grouped_swiglu_expert_gather": (ctypes.c_int,
+                                     [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_unpermute": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -116,8 +119,11 @@ def permute_workspace_bytes(T: int, k: int, E: int) -> int:
 
 
 def moe_permute(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int, *, x_perm=None, counts=None,
-                offsets=None, perm=None, inv_map=None, workspace=None) -> Permuted:
-    """Histogram, offsets, stable order, inverse map and permuted gather (one stream, no sync)."""
+                offsets=None, perm=None, inv_map=None, workspace=None, gather: bool = True) -> Permuted:
+    """Histogram, offsets, stable order, inverse map and permuted gather (one stream, no sync).
+
+    ``gather=False`` skips the row copy (``x_perm`` is None); a ``*_gather`` GEMM then reads X through perm.
+    """
     if x.dim() != 2 or expert_ids.dim() != 2:
         raise ValueError("x must be [T, d] and expert_ids [T, k]")
     T, d = x.shape
@@ -127,7 +133,7 @@ def moe_permute(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int, *, 
     _want(expert_ids, "expert_ids", torch.int32, (T, k), dev)
     S = T * k
     E = int(num_experts)
-    x_perm = _out(x_perm, "x_perm", torch.bfloat16, (S, d), dev)
+    x_perm = _out(x_perm, "x_perm", torch.bfloat16, (S, d), dev) if gather else None
     counts = _out(counts, "counts", torch.int32, (E,), dev)
     offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
     perm = _out(perm, "perm", torch.int32, (S,), dev)
@@ -137,7 +143,8 @@ def moe_permute(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int, *, 
         workspace = torch.empty((max(need, 4),), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
-    _check(load_library().moe_permute(_ptr(x), _ptr(expert_ids), T, k, d, E, _ptr(x_perm), _ptr(counts), _ptr(offsets),
+    _check(load_library().moe_permute(_ptr(x) if gather else None, _ptr(expert_ids), T, k, d, E, _ptr(x_perm),
+                                      _ptr(counts), _ptr(offsets),
                            _ptr(perm), _ptr(inv_map), _ptr(workspace), workspace.numel(), _stream(x)),
            "moe_permute")
     return Permuted(x_perm, counts, offsets, perm, inv_map)
@@ -161,6 +168,49 @@ def moe_gemm_up_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.
     _check(load_library().moe_gemm_up_swiglu(_ptr(x_perm), _ptr(offsets), _ptr(w_ug), cap, d, h, E, _ptr(h_buf),
                                   _stream(x_perm)), "moe_gemm_up_swiglu")
     return h_buf
+
+
+def moe_gemm_up_swiglu_gather(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.Tensor,
+                              k: int, *, h_buf=None) -> torch.Tensor:
+    """moe_gemm_up_swiglu on token rows gathered through perm: sorted row p reads x[perm[p] // k] (one launch)."""
+    if x.dim() != 2 or w_ug.dim() != 3:
+        raise ValueError("expected x [T, d] and w_ug [E, 2h, d]")
+    T, d = x.shape
+    E, two_h, _ = w_ug.shape
+    h = two_h // 2
+    S = T * int(k)
+    dev = x.device
+    _want(x, "x", torch.bfloat16, (T, d), dev)
+    _want(perm, "perm", torch.int32, (S,), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w_ug, "w_ug", torch.bfloat16, (E, 2 * h, d), dev)
+    h_buf = _out(h_buf, "h_buf", torch.bfloat16, (S, h), dev)
+    _check(load_library().moe_gemm_up_swiglu_gather(_ptr(x), _ptr(perm), T, int(k), _ptr(offsets), _ptr(w_ug), d, h,
+                                                    E, _ptr(h_buf), _stream(x)), "moe_gemm_up_swiglu_gather")
+    return h_buf
+
+
+def grouped_swiglu_expert_gather(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.Tensor,
+                                 w_down: torch.Tensor, k: int, *, h_buf=None, y_perm=None):
+    """grouped_swiglu_expert with the permuted gather fused into the gate/up loads: returns (h_buf, y_perm)."""
+    if x.dim() != 2 or w_ug.dim() != 3 or w_down.dim() != 3:
+        raise ValueError("expected x [T, d], w_ug [E, 2h, d], w_down [E, h, d]")
+    T, d = x.shape
+    E, two_h, _ = w_ug.shape
+    h = two_h // 2
+    S = T * int(k)
+    dev = x.device
+    _want(x, "x", torch.bfloat16, (T, d), dev)
+    _want(perm, "perm", torch.int32, (S,), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w_ug, "w_ug", torch.bfloat16, (E, 2 * h, d), dev)
+    _want(w_down, "w_down", torch.bfloat16, (E, h, d), dev)
+    h_buf = _out(h_buf, "h_buf", torch.bfloat16, (S, h), dev)
+    y_perm = _out(y_perm, "y_perm", torch.bfloat16, (S, d), dev)
+    _check(load_library().grouped_swiglu_expert_gather(_ptr(x), _ptr(perm), T, int(k), _ptr(offsets), _ptr(w_ug),
+                                                       _ptr(w_down), d, h, E, _ptr(h_buf), _ptr(y_perm), _stream(x)),
+           "grouped_swiglu_expert_gather")
+    return h_buf, y_perm
 
 
 def moe_gemm_down(h_buf: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, *, y_perm=None) -> torch.Tensor:
@@ -209,16 +259,23 @@ def moe_unpermute(y_perm: torch.Tensor, inv_map: torch.Tensor, routing_w: torch.
     return y
 
 
-def moe_expert_forward(x, expert_ids, routing_w, w_ug, w_down):
-    """The whole step: permute, grouped SwiGLU expert, unpermute. Returns (y, Permuted, h_buf, y_perm)."""
-    p = moe_permute(x, expert_ids, w_ug.shape[0])
-    h_buf, y_perm = grouped_swiglu_expert(p.x_perm, p.offsets, w_ug, w_down)
+def moe_expert_forward(x, expert_ids, routing_w, w_ug, w_down, fused_gather: bool = False):
+    """The whole step: permute, grouped SwiGLU expert, unpermute. Returns (y, Permuted, h_buf, y_perm).
+
+    ``fused_gather=True`` skips x_perm: the gate/up GEMM reads X through perm.
+    """
+    p = moe_permute(x, expert_ids, w_ug.shape[0], gather=not fused_gather)
+    if fused_gather:
+        h_buf, y_perm = grouped_swiglu_expert_gather(x, p.perm, p.offsets, w_ug, w_down, expert_ids.shape[1])
+    else:
+        h_buf, y_perm = grouped_swiglu_expert(p.x_perm, p.offsets, w_ug, w_down)
     y = moe_unpermute(y_perm, p.inv_map, routing_w)
     return y, p, h_buf, y_perm
 
 
 __all__ = [
     "LIB_PATH", "MAX_EXPERTS", "MoeError", "Permuted", "grouped_swiglu_expert", "header_functions", "load_library",
-    "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu", "moe_permute", "moe_unpermute",
+    "grouped_swiglu_expert_gather", "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu",
+    "moe_gemm_up_swiglu_gather", "moe_permute", "moe_unpermute",
     "permute_workspace_bytes",
 ]

@@ -68,7 +68,8 @@ moe_status moe_permute(const uint16_t* x, const int32_t* expert_ids, int64_t T, 
   if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS || bad_width(d) || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
   const int64_t S = T * k;
   const size_t need = moe_permute_workspace_bytes(T, k, E);
-  if (missing(x, T * d) || missing(expert_ids, S) || missing(x_perm, S * d) || missing(counts, E) ||
+  // x_perm == NULL asks for no row gather (a later *_gather GEMM reads x through perm); x is then unused.
+  if ((x_perm != nullptr && missing(x, T * d)) || missing(expert_ids, S) || missing(counts, E) ||
       missing(offsets, E + 1) || missing(perm, S) || missing(inv_map, S) || missing(workspace, (int64_t)need))
     return MOE_ERR_NULL_POINTER;
   if (misaligned(x, 16) || misaligned(x_perm, 16) || misaligned(expert_ids, 4) || misaligned(counts, 4) ||
@@ -97,6 +98,25 @@ moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, co
   return launched(launch_gemm_up_swiglu(x_perm, offsets, w_ug, cap_rows, d, h, E, h_buf, stream));
 }
 
+moe_status moe_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
+                                     const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
+                                     uint16_t* h_buf, hipStream_t stream) {
+  if (T < 0 || k < 1 || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  moe_status st = check_gemm_shape(S, d, h, E);
+  if (st != MOE_OK) return st;
+  if (missing(x, T * d) || missing(perm, S) || missing(offsets, E + 1) || missing(w_ug, (int64_t)E * 2 * h * d) ||
+      missing(h_buf, S * h))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x, 16) || misaligned(w_ug, 16) || misaligned(h_buf, 16) || misaligned(offsets, 4) ||
+      misaligned(perm, 4))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  if (S == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_gemm_up_swiglu_gather(x, perm, T, k, offsets, w_ug, d, h, E, h_buf, stream));
+}
+
 moe_status moe_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down, int64_t cap_rows,
                          int64_t d, int64_t h, int32_t E, uint16_t* y_perm, hipStream_t stream) {
   moe_status st = check_gemm_shape(cap_rows, d, h, E);
@@ -122,6 +142,21 @@ moe_status grouped_swiglu_expert(const uint16_t* x_perm, const int32_t* offsets,
   st = moe_gemm_up_swiglu(x_perm, offsets, w_ug, cap_rows, d, h, E, h_buf, stream);
   if (st != MOE_OK) return st;
   return moe_gemm_down(h_buf, offsets, w_down, cap_rows, d, h, E, y_perm, stream);
+}
+
+moe_status grouped_swiglu_expert_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
+                                        const int32_t* offsets, const uint16_t* w_ug, const uint16_t* w_down,
+                                        int64_t d, int64_t h, int32_t E, uint16_t* h_buf, uint16_t* y_perm,
+                                        hipStream_t stream) {
+  if (T < 0 || k < 1 || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  moe_status st = check_gemm_shape(S, d, h, E);
+  if (st != MOE_OK) return st;
+  if (missing(w_down, (int64_t)E * h * d) || missing(y_perm, S * d)) return MOE_ERR_NULL_POINTER;
+  if (misaligned(w_down, 16) || misaligned(y_perm, 16)) return MOE_ERR_MISALIGNED;
+  st = moe_gemm_up_swiglu_gather(x, perm, T, k, offsets, w_ug, d, h, E, h_buf, stream);
+  if (st != MOE_OK) return st;
+  return moe_gemm_down(h_buf, offsets, w_down, S, d, h, E, y_perm, stream);
 }
 
 moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const float* routing_w, int64_t T, int32_t k,

@@ -73,8 +73,11 @@ struct Tile {
 };
 
 struct GemmArgs {
-  const uint16_t* A;        // activations [cap_rows, K], row pitch lda
+  const uint16_t* A;        // activations: [cap_rows, K], or token rows [a_tokens, K] when a_rows is set
   int64_t lda;
+  const int32_t* a_rows;    // optional: sorted row p reads A row a_rows[p] / a_k (the fused permuted gather)
+  int a_k;
+  int64_t a_tokens;
   const uint16_t* W;        // expert weights
   int64_t w_expert_stride;  // elements between experts
   int64_t ldw;              // row pitch of a weight matrix
@@ -144,6 +147,16 @@ __device__ __forceinline__ int logical_worker() {
   const int G = gridDim.x, b = blockIdx.x;
   if (G % 8 != 0) return b;
   return (b % 8) * (G / 8) + b / 8;
+}
+
+// A row feeding sorted row p: p itself, or (fused gather) the token of dispatch
+// slot a_rows[p], clamped into the token range.
+__device__ __forceinline__ int64_t a_row_of(const GemmArgs& g, int64_t p) {
+  if (g.a_rows == nullptr) return p;
+  int64_t slot = g.a_rows[p];
+  const int64_t cap = g.a_tokens * g.a_k;
+  slot = slot < 0 ? 0 : (slot >= cap ? cap - 1 : slot);
+  return slot / g.a_k;
 }
 
 // Problem list from the device offsets, clamped so no access leaves the buffers:
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
       const int r = 8 * j + (lane >> 3);
       const int c = swz(r, lane & 7);  // the swizzle is an involution: position -> logical chunk
       const int rr = r < tc.rows_valid ? r : tc.rows_valid - 1;
-      a_src[t2] = g.A + (tc.row0 + rr) * g.lda + c * 8;
+      a_src[t2] = g.A + a_row_of(g, tc.row0 + rr) * g.lda + c * 8;
     }
     const uint16_t* b_src[C::B_OPS];
 #pragma unroll
@@ -487,7 +500,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs 
         const int r = idx / kChunksK, c = idx % kChunksK;
         const int64_t kk = k0 + c * 8;
         ra[i] = (r < tc.rows_valid && kk < g.K)
-                    ? *reinterpret_cast<const u32x4*>(g.A + (tc.row0 + r) * g.lda + kk)
+                    ? *reinterpret_cast<const u32x4*>(g.A + a_row_of(g, tc.row0 + r) * g.lda + kk)
                     : zero4();
       }
     };
@@ -651,14 +664,22 @@ hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets,
                                  int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
                                  hipStream_t stream) {
   // A = x_perm [cap, d] (K = d); weights [E, 2h, d], gate rows n, up rows h + n; out h_buf [cap, h]
-  const GemmArgs g{x_perm, d, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h};
+  const GemmArgs g{x_perm, d, nullptr, 1, 0, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h};
+  return launch_grouped<true, false>(g, stream);
+}
+
+hipError_t launch_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
+                                        const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
+                                        uint16_t* h_buf, hipStream_t stream) {
+  // A rows are gathered: sorted row p reads x[perm[p] / k]
+  const GemmArgs g{x, d, perm, k, T, w_ug, 2 * h * d, d, h, h, d, offsets, E, T * k, h_buf, h};
   return launch_grouped<true, false>(g, stream);
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down, int64_t cap_rows,
                             int64_t d, int64_t h, int32_t E, uint16_t* y_perm, hipStream_t stream) {
   // A = h_buf [cap, h] (K = h); weights [E, h, d] N-contiguous; out y_perm [cap, d]
-  const GemmArgs g{h_buf, h, w_down, h * d, d, 0, d, h, offsets, E, cap_rows, y_perm, d};
+  const GemmArgs g{h_buf, h, nullptr, 1, 0, w_down, h * d, d, 0, d, h, offsets, E, cap_rows, y_perm, d};
   return launch_grouped<false, true>(g, stream);
 }
 

@@ -213,7 +213,7 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int3
   hipLaunchKernelGGL(colscan_kernel, dim3(E), dim3(kScanThreads), 0, stream, table, nchunks, counts);
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(nchunks > 0 ? nchunks : 1)), dim3(64), 0, stream, ids, S, E,
                      bits_for(E), counts, table, nchunks, offsets, perm, inv);
-  if (S > 0) {
+  if (S > 0 && x_perm != nullptr) {  // no x_perm: the caller gathers inside the GEMM
     const int dev = current_device();
     const int64_t cpr = d / 8;
     const int64_t rpi = cpr <= kGatherThreads ? kGatherThreads / cpr : 1;

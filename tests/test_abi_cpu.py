@@ -55,7 +55,7 @@ def permute(lib, T=4, k=2, d=8, E=4, x=FAKE, ids=FAKE, xp=FAKE, counts=FAKE, off
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(E=0), SHAPE), (dict(E=1025), SHAPE), (dict(d=12), SHAPE),
     (dict(d=0), SHAPE), (dict(T=2**31, k=1), SHAPE), (dict(T=2**30, k=2), SHAPE),
-    (dict(x=None), NULLP), (dict(ids=None), NULLP), (dict(xp=None), NULLP), (dict(counts=None), NULLP),
+    (dict(x=None), NULLP), (dict(ids=None), NULLP), (dict(counts=None), NULLP),
     (dict(offs=None), NULLP), (dict(perm=None), NULLP), (dict(inv=None), NULLP), (dict(ws=None), NULLP),
     (dict(x=FAKE + 8), ALIGN), (dict(xp=FAKE + 2), ALIGN), (dict(ids=FAKE + 2), ALIGN), (dict(inv=FAKE + 1), ALIGN),
     (dict(wsb=3), WS),
@@ -83,6 +83,24 @@ def gemm(lib, fn, cap=16, d=16, h=16, E=2, a=FAKE, offs=FAKE, w=FAKE, out=FAKE):
 ])
 def test_gemm_validation(lib, fn, kw, status):
     assert gemm(lib, fn, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(d=12), SHAPE), (dict(E=0), SHAPE), (dict(T=2**30, k=2), SHAPE),
+    (dict(x=None), NULLP), (dict(perm=None), NULLP), (dict(offs=None), NULLP), (dict(w=None), NULLP),
+    (dict(out=None), NULLP), (dict(x=FAKE + 8), ALIGN), (dict(perm=FAKE + 2), ALIGN), (dict(out=FAKE + 4), ALIGN),
+])
+def test_gather_gemm_validation(lib, kw, status):
+    a = dict(x=FAKE, perm=FAKE, T=8, k=2, offs=FAKE, w=FAKE, d=16, h=16, E=2, out=FAKE)
+    a.update(kw)
+    assert lib.moe_gemm_up_swiglu_gather(a["x"], a["perm"], a["T"], a["k"], a["offs"], a["w"], a["d"], a["h"],
+                                         a["E"], a["out"], None) == status
+
+
+def test_permute_without_gather_needs_no_rows(lib):
+    # x_perm = NULL: no row copy, so x may be NULL too; everything else is still required
+    assert permute(lib, x=None, xp=None) in (OK, DEV)
+    assert permute(lib, x=None, xp=None, perm=None) == NULLP
 
 
 def test_grouped_validation_checks_both_halves(lib):

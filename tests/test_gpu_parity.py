@@ -23,9 +23,9 @@ pytestmark = pytest.mark.gpu
 NAMES = list(WORKLOADS)
 
 
-def run_path(wl, sync=True):
+def run_path(wl, sync=True, fused=False):
     di = DeviceInputs(wl)
-    y, p, h_buf, y_perm = moe.moe_expert_forward(di.x, di.ids, di.w, di.w_ug, di.w_down)
+    y, p, h_buf, y_perm = moe.moe_expert_forward(di.x, di.ids, di.w, di.w_ug, di.w_down, fused_gather=fused)
     if sync:
         torch.cuda.synchronize()
     return y, p, h_buf, y_perm
@@ -37,7 +37,8 @@ def check_permute(p, ref, wl):
     np.testing.assert_array_equal(p.offsets.cpu().numpy(), ref.offsets)
     np.testing.assert_array_equal(p.perm.cpu().numpy()[:M], ref.perm[:M])
     np.testing.assert_array_equal(p.inv_map.cpu().numpy(), ref.inv_map)
-    np.testing.assert_array_equal(bits(p.x_perm)[:M], ref.x_perm)
+    if p.x_perm is not None:  # the fused-gather path never materialises x_perm
+        np.testing.assert_array_equal(bits(p.x_perm)[:M], ref.x_perm)
 
 
 def check_all(wl, ref, y, p, h_buf, y_perm):
@@ -51,11 +52,12 @@ def check_all(wl, ref, y, p, h_buf, y_perm):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", NAMES)
-def test_named_workload_full_size(name):
+@pytest.mark.parametrize("name,fused", [(n, f) for n in NAMES for f in (False, True)],
+                         ids=[f"{n}-{'fused' if f else 'xperm'}" for n in NAMES for f in (False, True)])
+def test_named_workload_full_size(name, fused):
     wl = workload(name)
-    say(f"[gpu] full path {name}")
-    y, p, h_buf, y_perm = run_path(wl)
+    say(f"[gpu] full path {name} fused_gather={fused}")
+    y, p, h_buf, y_perm = run_path(wl, fused=fused)
     ref = oracle_result(name)
     check_all(wl, ref, y, p, h_buf, y_perm)
 
@@ -99,6 +101,10 @@ def test_random_cases(case):
     y, p, h_buf, y_perm = run_path(wl)
     ref = oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
     check_all(wl, ref, y, p, h_buf, y_perm)
+    # the fused-gather path runs the same arithmetic on the same rows: identical bits
+    y2, p2, h2, yp2 = run_path(wl, fused=True)
+    M = ref.M
+    assert torch.equal(y2, y) and torch.equal(h2[:M], h_buf[:M]) and torch.equal(yp2[:M], y_perm[:M])
 
 
 def test_negative_controls_fail_the_comparison():
