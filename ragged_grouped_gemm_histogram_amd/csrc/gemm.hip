@@ -635,12 +635,12 @@ hipError_t launch_kernel(Kern kern, bool* attr_done, const GemmArgs& g, hipStrea
 // Tile configurations. Large expert blocks (mean rows per expert >= 384) take
 // 256 x 256 tiles on 8 waves (two per SIMD, so one wave's LDS and barrier waits
 // overlap the other's MFMAs) with a 2-stage ring; smaller blocks take 128 x 256
-// tiles on 4 waves with a 3-stage ring, which wastes fewer rows on ragged
+// tiles on 8 waves with a 3-stage ring, which wastes fewer rows on ragged
 // tails. K not a multiple of 64 takes the register-staged loop.
 template <bool GATED>
 using BigTile = Tile<256, 256, 2, 4, 2, GATED>;
 template <bool GATED>
-using SmallTile = Tile<128, 256, 2, 2, 3, GATED>;
+using SmallTile = Tile<128, 256, 2, 4, 3, GATED>;
 template <bool GATED>
 using RegsTile = Tile<128, 256, 2, 2, 2, GATED>;
 
