@@ -101,6 +101,11 @@ def main(argv=None):
                     help="copy rows into x_perm in moe_permute instead of gathering them inside the gate/up GEMM")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--sweep", choices=SWEEPS,
+                    help="instead of the step, run one single-projection sweep and print its own JSON line: "
+                         "histogram (Fig 40), capacity (Fig 38) or decomposition (Fig 39)")
+    ap.add_argument("--sweep-samples", type=int, default=20, help="timed samples per sweep point")
+    ap.add_argument("--sweep-warmup", type=int, default=10, help="warm-up samples per sweep point")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +122,9 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        print(json.dumps(SWEEPS[args.sweep](torch, moe, dev, args.sweep_warmup, args.sweep_samples)))
+        return 0
     wl = make_workload(args.config)
     T, k, E, d, h = wl.T, wl.k, wl.E, wl.d, wl.h
     S = T * k
@@ -314,6 +322,227 @@ def run_variants(torch, moe, x, ids, rw, w_ug, w_down, wl, counts, offsets, x_pe
                           "padding_fraction_executed": 1 - kept_rows / (E * C)})
         res[name] = entry
     return res
+
+
+# --------------------------------------------------------------------------
+# Single-projection sweeps (OLMo report Sec 9.6): one grouped projection
+# Y[rows_e] = A[rows_e] @ W[e] (moe_gemm_down), 16 local experts unless stated.
+# --------------------------------------------------------------------------
+
+
+def _progress(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class QueuedTimer:
+    """Fig 38's protocol: warm-up and timed samples are all queued behind a device-side gate (a
+    spin kernel of fixed length) and released together, so host launch gaps never reach the GPU;
+    each timed sample is bracketed by HIP events on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        self.cycles_per_ms = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+        self.gate_overruns = 0
+
+    def __call__(self, fn, warmup: int, samples: int, gate_ms: float = 30.0):
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+        gate_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        torch.cuda._sleep(int(gate_ms * self.cycles_per_ms))
+        gate_end.record()
+        for _ in range(warmup):
+            fn()
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        queued_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        if queued_ms > gate_ms:  # the gate opened before the host finished queuing
+            self.gate_overruns += 1
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return {"mean_ms": sum(ts) / len(ts), "median_ms": ts[len(ts) // 2], "min_ms": ts[0]}
+
+
+def _offsets_dev(torch, counts, dev):
+    import numpy as np
+
+    offs = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))]).astype(np.int32)
+    return torch.from_numpy(offs).to(dev)
+
+
+def sweep_histogram(torch, moe, dev, warmup, samples):
+    """Fig 40: fixed rows and FLOPs, 100 load histograms spanning Eq 18's imbalance range.
+
+    Each histogram is timed under four fixed expert-index orders; conditions run in a seeded
+    random order, and a balanced control is timed before the first and after every ten
+    conditions. A condition's relative throughput is the mean of its two bracketing controls'
+    times over its own time; a histogram's value is the mean over its four orders."""
+    import numpy as np
+    from scipy.stats import spearmanr
+
+    from workloads import SWEEP, balanced_counts, dirichlet_histograms, expert_orders, projection_inputs
+
+    E, M, dim = SWEEP["E"], SWEEP["M"], SWEEP["dim"]
+    a, w = projection_inputs(M, dim, dim, E, seed=40, device=dev)
+    y = torch.empty((M, dim), dtype=torch.bfloat16, device=dev)
+    hists = dirichlet_histograms()
+    orders = expert_orders(E, 4)
+    conds = []
+    for hi, hrec in enumerate(hists):
+        for oi, order in enumerate(orders):
+            per_expert = np.empty(E, dtype=np.int64)
+            per_expert[order] = hrec["counts"]  # expert order[i] gets the i-th count
+            conds.append((hi, oi, _offsets_dev(torch, per_expert, dev)))
+    rng = np.random.default_rng(42)
+    conds = [conds[i] for i in rng.permutation(len(conds))]
+    bal = _offsets_dev(torch, balanced_counts(E, M), dev)
+    timer = QueuedTimer(torch)
+
+    def run(offs):
+        return timer(lambda: moe.moe_gemm_down(a, offs, w, y_perm=y), warmup, samples)["mean_ms"]
+
+    controls = [run(bal)]
+    times = []
+    for i, (hi, oi, offs) in enumerate(conds):
+        times.append(run(offs))
+        if (i + 1) % 10 == 0 or i + 1 == len(conds):
+            controls.append(run(bal))
+            _progress(f"histogram sweep: {i + 1}/{len(conds)} conditions, control {controls[-1]:.3f} ms")
+    rel = np.zeros((len(hists), len(orders)))
+    ms = np.zeros((len(hists), len(orders)))
+    for i, (hi, oi, _) in enumerate(conds):
+        c = 0.5 * (controls[i // 10] + controls[i // 10 + 1])
+        rel[hi, oi] = c / times[i]
+        ms[hi, oi] = times[i]
+    rel_h = rel.mean(axis=1)
+    imb = np.array([h["imbalance"] for h in hists])
+    rho = float(spearmanr(imb, rel_h).statistic)
+    boot = []
+    brng = np.random.default_rng(43)
+    for _ in range(2000):
+        idx = brng.integers(0, len(hists), len(hists))
+        boot.append(spearmanr(imb[idx], rel_h[idx]).statistic)
+    lo, hi_ = np.nanpercentile(boot, [2.5, 97.5])
+    flops = 2 * M * dim * dim
+    bal_ms = float(np.mean(controls))
+    bins = sorted({h["bin"] for h in hists})
+    medians = [{"bin": b, "imbalance_median": float(np.median(imb[[h["bin"] == b for h in hists]])),
+                "rel_median": float(np.median(rel_h[[h["bin"] == b for h in hists]]))} for b in bins]
+    return {
+        "metric": "grouped projection throughput relative to balanced load vs imbalance I_H (Eq 18)",
+        "sweep": "histogram", "unit": "ratio", "data": "synthetic", "dtype": "bf16",
+        "config": {"workload": "histogram sweep", "E": E, "M": M, "d": dim, "h": dim, "align": SWEEP["align"],
+                   "min_rows": SWEEP["min_rows"], "histograms": len(hists), "orders": len(orders),
+                   "warmup": warmup, "samples": samples, "kernel": "moe_gemm_down"},
+        "balanced_ms": bal_ms, "balanced_TFLOP/s": flops / bal_ms / 1e9,
+        "controls_ms_min_max": [float(min(controls)), float(max(controls))],
+        "spearman_rho": rho, "bootstrap_95": [float(lo), float(hi_)],
+        "bin_medians": medians, "gate_overruns": timer.gate_overruns,
+        "histograms": [{"imbalance": float(imb[i]), "alpha": float(hists[i]["alpha"]),
+                        "counts_sorted": sorted(hists[i]["counts"].tolist(), reverse=True),
+                        "rel": float(rel_h[i]), "rel_by_order": [float(v) for v in rel[i]],
+                        "ms": float(ms[i].mean())} for i in range(len(hists))],
+    }
+
+
+def sweep_capacity(torch, moe, dev, warmup, samples):
+    """Fig 38: exact-row grouped projection vs a batched GEMM padded to 1.25x the mean load, across
+    total routed rows M with balanced routing (M/16 rows per expert); kernel time only, the padded
+    operand built before timing. Useful FLOPs count valid rows only, 2*M*d*h."""
+    from workloads import balanced_counts, projection_inputs
+
+    E, dim = 16, 4096
+    Ms = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
+    a, w = projection_inputs(max(Ms), dim, dim, E, seed=38, device=dev)
+    y = torch.empty((max(Ms), dim), dtype=torch.bfloat16, device=dev)
+    timer = QueuedTimer(torch)
+    points = []
+    for M in Ms:
+        counts = balanced_counts(E, M)
+        offs = _offsets_dev(torch, counts, dev)
+        C = math.ceil(1.25 * M / E)
+        pad = torch.zeros((E, C, dim), dtype=torch.bfloat16, device=dev)
+        lo = 0
+        for e in range(E):
+            pad[e, :counts[e]] = a[lo:lo + counts[e]]
+            lo += int(counts[e])
+        out = torch.empty((E, C, dim), dtype=torch.bfloat16, device=dev)
+        am = a[:M]
+        ym = y[:M]
+        g = timer(lambda: moe.moe_gemm_down(am, offs, w, y_perm=ym), warmup, samples)
+        b = timer(lambda: torch.bmm(pad, w, out=out), warmup, samples)
+        flops = 2 * M * dim * dim
+        points.append({"M": M, "rows_per_expert": M // E, "C": C,
+                       "grouped_ms": g["mean_ms"], "bmm_ms": b["mean_ms"],
+                       "grouped_TFLOP/s": flops / g["mean_ms"] / 1e9, "bmm_useful_TFLOP/s": flops / b["mean_ms"] / 1e9,
+                       "bmm_padded_TFLOP/s": 2 * E * C * dim * dim / b["mean_ms"] / 1e9,
+                       "bmm_over_grouped_time": b["mean_ms"] / g["mean_ms"],
+                       "grouped_median_ms": g["median_ms"], "bmm_median_ms": b["median_ms"]})
+        del pad, out
+        _progress(f"capacity sweep: M={M} grouped {g['mean_ms']:.4f} ms, bmm {b['mean_ms']:.4f} ms")
+    cross = next((p["M"] for p in points if p["bmm_over_grouped_time"] > 1.0), None)
+    return {"metric": "useful TFLOP/s of one grouped projection vs padded BMM at 1.25x capacity, across M",
+            "sweep": "capacity", "unit": "TFLOP/s", "data": "synthetic", "dtype": "bf16",
+            "config": {"workload": "capacity sweep", "E": E, "d": dim, "h": dim, "capacity_factor": 1.25,
+                       "warmup": warmup, "samples": samples, "kernel": "moe_gemm_down", "bmm": "torch.bmm"},
+            "first_M_grouped_faster": cross, "gate_overruns": timer.gate_overruns, "points": points}
+
+
+def sweep_decomposition(torch, moe, dev, warmup, samples):
+    """Fig 39 / Eq 17: one dense [T, 8192] @ [8192, 81920] projection vs the same weight split into
+    4 or 8 column-block experts, each multiplying the whole input (the input repeated once per
+    expert). Dense runs twice: the vendor GEMM (torch.matmul) and this library with one expert."""
+    from workloads import projection_inputs
+
+    K, N = 8192, 81920
+    Ts = [1, 16, 128, 256, 1024, 4096, 8192, 16384, 32768, 65536]
+    x_all, w1 = projection_inputs(max(Ts), K, N, 1, seed=39, device=dev)
+    wd = w1[0]  # [K, N]
+    blocks = {n: wd.view(K, n, N // n).permute(1, 0, 2).contiguous() for n in (4, 8)}  # [n, K, N/n]
+    timer = QueuedTimer(torch)
+    points = []
+    for T in Ts:
+        x = x_all[:T]
+        flops = 2 * T * K * N
+        res = {"T": T}
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        r = timer(lambda: torch.matmul(x, wd, out=out), warmup, samples)
+        res["dense_vendor_TFLOP/s"] = flops / r["mean_ms"] / 1e9
+        res["dense_vendor_ms"] = r["mean_ms"]
+        offs1 = _offsets_dev(torch, [T], dev)
+        r = timer(lambda: moe.moe_gemm_down(x, offs1, w1, y_perm=out), warmup, samples)
+        res["dense_ours_TFLOP/s"] = flops / r["mean_ms"] / 1e9
+        res["dense_ours_ms"] = r["mean_ms"]
+        del out
+        for n, wb in blocks.items():
+            xr = x.repeat(n, 1)
+            yb = torch.empty((n * T, N // n), dtype=torch.bfloat16, device=dev)
+            offs = _offsets_dev(torch, [T] * n, dev)
+            r = timer(lambda: moe.moe_gemm_down(xr, offs, wb, y_perm=yb), warmup, samples)
+            res[f"grouped{n}_TFLOP/s"] = flops / r["mean_ms"] / 1e9
+            res[f"grouped{n}_ms"] = r["mean_ms"]
+            res[f"grouped{n}_over_dense_vendor"] = res[f"grouped{n}_TFLOP/s"] / res["dense_vendor_TFLOP/s"]
+            del xr, yb
+        points.append(res)
+        _progress(f"decomposition sweep: T={T} " + ", ".join(f"{k} {v:.1f}" for k, v in res.items() if "TFLOP" in k))
+    return {"metric": "useful TFLOP/s of one dense projection vs 4 and 8 column-block experts (Eq 17)",
+            "sweep": "decomposition", "unit": "TFLOP/s", "data": "synthetic", "dtype": "bf16",
+            "config": {"workload": "decomposition sweep", "K": K, "N": N, "experts": [4, 8], "warmup": warmup,
+                       "samples": samples, "kernel": "moe_gemm_down", "dense_vendor": "torch.matmul"},
+            "gate_overruns": timer.gate_overruns, "points": points}
+
+
+SWEEPS = {"histogram": sweep_histogram, "capacity": sweep_capacity, "decomposition": sweep_decomposition}
 
 
 if __name__ == "__main__":

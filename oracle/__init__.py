@@ -36,6 +36,7 @@ from .moe import (
     entropy_deficit,
     exclusive_offsets,
     expert_forward,
+    grouped_projection,
     moe_expert_forward,
     padding_fraction,
     permute_rows,

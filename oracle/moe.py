@@ -174,6 +174,36 @@ def expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision: str 
     return h_out, y_out
 
 
+def grouped_projection(a_bits, offsets, w_bits, precision: str = "f64") -> np.ndarray:
+    """One grouped expert projection: ``Y[rows_e] = bf16(A[rows_e] @ W[e])`` per expert.
+
+    The single-projection problem the OLMo report measures in Sec 9.6 (Figs 38
+    and 40: one square bf16 expert projection per local expert over its own
+    rows; Fig 39 / Eq 17: the experts' weights are column blocks of one dense
+    weight). ``a_bits`` uint16 [>= M, K], ``offsets`` int [E+1], ``w_bits``
+    uint16 [E, K, N] (row-major, the layout of a down projection). Rows of an
+    expert with no rows are never touched. Returns uint16 [M, N].
+    """
+    ft = _ftype(precision)
+    offsets = np.asarray(offsets).astype(np.int64)
+    E = offsets.shape[0] - 1
+    M = int(offsets[E])
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    if w_bits.ndim != 3 or w_bits.shape[0] != E:
+        raise ValueError(f"w must be [E={E}, K, N], got {w_bits.shape}")
+    N = w_bits.shape[2]
+    a_bits = np.asarray(a_bits, dtype=np.uint16)
+    out = np.zeros((M, N), dtype=np.uint16)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        a = bf16_bits_to_f64(a_bits[lo:hi]).astype(ft)
+        w = bf16_bits_to_f64(w_bits[e]).astype(ft)
+        out[lo:hi] = f64_to_bf16_bits(np.matmul(a, w))
+    return out
+
+
 # --------------------------------------------------------------------------
 # Scatter-back: atomic-free unpermute through the inverse map
 # --------------------------------------------------------------------------

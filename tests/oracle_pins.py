@@ -279,6 +279,56 @@ def pin_token_form(orc) -> None:
     _assert_close_bits(rows, r.y, "token form", min_exact=0.99, max_ulp=1)
 
 
+def pin_projection_column_partition(orc) -> None:
+    """Eq 17 for one projection: the experts' weights are column blocks of one dense weight and
+    every expert multiplies the same rows, so the grouped outputs, laid side by side, are the
+    dense product (torch float64 matmul, torch bf16 rounding)."""
+    rng = np.random.default_rng(13)
+    T, K, N, E = 24, 40, 48, 4  # K != N / E: a transposed block cannot type-check
+    x = to_bf16_bits(rng.standard_normal((T, K), dtype=np.float32))
+    w = to_bf16_bits(0.2 * rng.standard_normal((K, N), dtype=np.float32))
+    nb = N // E
+    blocks = np.stack([w[:, e * nb:(e + 1) * nb] for e in range(E)])  # [E, K, N/E]
+    a = np.concatenate([x] * E, axis=0)  # the input repeated once per expert
+    offsets = np.arange(E + 1, dtype=np.int32) * T
+    got = orc.grouped_projection(a, offsets, blocks)
+    side = np.concatenate([got[e * T:(e + 1) * T] for e in range(E)], axis=1)  # [T, N]
+    dense = _torch_bf16_bits(_bits_to_f64(x) @ _bits_to_f64(w))
+    _assert_close_bits(side, dense, "Eq 17 projection partition", min_exact=0.999, max_ulp=1)
+
+
+def pin_projection_brute_force(orc) -> None:
+    """Pure-Python loops over every output of a ragged grouped projection with an empty expert."""
+    rng = np.random.default_rng(17)
+    K, N = 6, 10
+    counts = [3, 0, 5, 1]
+    E = len(counts)
+    M = sum(counts)
+    a = to_bf16_bits(rng.standard_normal((M + 2, K), dtype=np.float32))  # two rows past M stay unused
+    w = to_bf16_bits(rng.standard_normal((E, K, N), dtype=np.float32))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    got = orc.grouped_projection(a, offsets, w)
+    av = _bits_to_f64(a).tolist()
+    wv = _bits_to_f64(w).tolist()
+    ref = np.zeros((M, N), dtype=np.uint16)
+    row = 0
+    for e, c in enumerate(counts):
+        for _ in range(c):
+            vals = [sum(av[row][q] * wv[e][q][n] for q in range(K)) for n in range(N)]
+            ref[row] = _torch_bf16_bits(torch.tensor(vals, dtype=torch.float64))
+            row += 1
+    _assert_close_bits(got, ref, "projection brute force", min_exact=1.0, max_ulp=0)
+
+
+def pin_projection_is_down_step(orc) -> None:
+    """The down projection inside the expert step is the grouped projection of H (same rows,
+    same weights, one bf16 rounding)."""
+    wl = make_random(T=30, k=2, E=5, d=48, h=32, seed=61, drop_frac=0.1, w_sigma=0.1, empty_experts=(3,))
+    r = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
+    y = orc.grouped_projection(r.h, r.offsets, wl.w_down)
+    np.testing.assert_array_equal(y, r.y_perm)
+
+
 ALL_PINS = [
     pin_toy_golden,
     pin_printed_arithmetic,
@@ -290,4 +340,7 @@ ALL_PINS = [
     pin_invariances,
     pin_f32_within_bound,
     pin_token_form,
+    pin_projection_column_partition,
+    pin_projection_brute_force,
+    pin_projection_is_down_step,
 ]

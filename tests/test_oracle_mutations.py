@@ -75,6 +75,34 @@ def _truncate_bf16(x):
     return ((x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)).astype(np.float64)
 
 
+_orig_projection = om.grouped_projection
+
+
+def _projection_shifted(a_bits, offsets, w_bits, precision="f64"):
+    # wrong weight index: expert e multiplied by expert (e+1)'s weights
+    return _orig_projection(a_bits, offsets, np.roll(np.asarray(w_bits), -1, axis=0), precision)
+
+
+def _projection_rows_shifted(a_bits, offsets, w_bits, precision="f64"):
+    # off-by-one segment: every expert's block starts one row late
+    offs = np.asarray(offsets).astype(np.int64).copy()
+    offs[1:-1] += 1
+    offs = np.minimum(offs, offs[-1])
+    return _orig_projection(a_bits, offs, w_bits, precision)
+
+
+def _projection_unrounded(a_bits, offsets, w_bits, precision="f64"):
+    # the stored Y left in a truncating conversion instead of round-to-nearest-even
+    offsets = np.asarray(offsets).astype(np.int64)
+    out = np.zeros((int(offsets[-1]), np.asarray(w_bits).shape[2]), dtype=np.uint16)
+    for e in range(offsets.shape[0] - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y = bf16_bits_to_f64(np.asarray(a_bits)[lo:hi]) @ bf16_bits_to_f64(np.asarray(w_bits)[e])
+            out[lo:hi] = (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return out
+
+
 MUTATIONS = {
     "silu_sign": [("_swiglu_expert", _swiglu_variant(silu_sign=-1.0))],
     "gate_up_swapped": [("_swiglu_expert", _swiglu_variant(gate_up_swapped=True))],
@@ -87,6 +115,9 @@ MUTATIONS = {
     "inclusive_offsets": [("exclusive_offsets", _offsets_inclusive)],
     "weights_ignored": [("unpermute", _unpermute_unweighted)],
     "truncating_rounding": [("round_to_bf16", _truncate_bf16)],
+    "projection_wrong_expert": [("grouped_projection", _projection_shifted)],
+    "projection_rows_shifted": [("grouped_projection", _projection_rows_shifted)],
+    "projection_truncated": [("grouped_projection", _projection_unrounded)],
 }
 
 

@@ -28,7 +28,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_workload", "make_random", "to_bf16_bits"]
+__all__ = ["Workload", "WORKLOADS", "make_workload", "make_random", "to_bf16_bits", "dirichlet_histograms",
+           "balanced_counts", "expert_orders", "imbalance_index", "projection_inputs", "SWEEP"]
 
 
 def to_bf16_bits(x_f32: np.ndarray) -> np.ndarray:
@@ -189,3 +190,124 @@ def make_random(T: int, k: int, E: int, d: int, h: int, seed: int, drop_frac: fl
         flat = ids.reshape(-1)
         flat[mask] = bad[mask].astype(np.int32)
     return _finish(rng, name, T, k, E, d, h, ids, w, x_sigma, w_sigma, f"random T={T} k={k} E={E} d={d} h={h}")
+
+
+# --------------------------------------------------------------------------
+# Inputs of the single-projection sweeps (OLMo report, Sec 9.6, Figs 38-40)
+# --------------------------------------------------------------------------
+
+# Fig 40's fixed-work histogram sweep: 16 local experts, M = 65,536 rows, one
+# square projection with d = h = 4096; counts are multiples of 8 rows and every
+# expert keeps at least one 128-row tile.
+SWEEP = {"E": 16, "M": 65536, "dim": 4096, "align": 8, "min_rows": 128, "n_bins": 10, "per_bin": 10}
+
+
+def balanced_counts(E: int, M: int) -> np.ndarray:
+    """M rows split as evenly as possible over E experts (the first M % E experts get one more)."""
+    base, extra = divmod(int(M), int(E))
+    return np.array([base + (1 if e < extra else 0) for e in range(E)], dtype=np.int64)
+
+
+def imbalance_index(counts) -> float:
+    """Normalised entropy deficit of a histogram, used here only to bin proposals.
+
+    The same statistic as the OLMo report's Eq 18; the test suite checks this
+    copy against the oracle's.
+    """
+    c = np.asarray(counts, dtype=np.float64)
+    n, tot = c.shape[0], c.sum()
+    if n <= 1 or tot == 0:
+        return 0.0
+    q = c[c > 0] / tot
+    return float(1.0 + np.sum(q * np.log(q)) / np.log(n))
+
+
+def _counts_from_proposal(p: np.ndarray, M: int, align: int, min_rows: int) -> np.ndarray:
+    """Exact counts from a probability vector: every expert keeps ``min_rows``; the remaining
+    M - E*min_rows rows are dealt in ``align``-row units by largest remainder."""
+    E = p.shape[0]
+    units = (M - E * min_rows) // align
+    raw = p * units
+    base = np.floor(raw).astype(np.int64)
+    short = units - int(base.sum())
+    if short > 0:
+        order = np.argsort(-(raw - base), kind="stable")
+        base[order[:short]] += 1
+    return min_rows + align * base
+
+
+def dirichlet_histograms(E: int = SWEEP["E"], M: int = SWEEP["M"], align: int = SWEEP["align"],
+                         min_rows: int = SWEEP["min_rows"], n_bins: int = SWEEP["n_bins"],
+                         per_bin: int = SWEEP["per_bin"], seed: int = 40, log10_alpha=(-3.0, 2.0),
+                         max_draws: int = 500_000) -> list[dict]:
+    """Fixed-work load histograms spanning the imbalance range (Fig 40's construction).
+
+    Symmetric-Dirichlet proposals, concentration alpha drawn log-uniformly
+    from ``10**log10_alpha``, are turned into exact counts (multiples of
+    ``align``, at least ``min_rows`` each, summing to M). The imbalance range
+    [0, I_max], where I_max belongs to the most concentrated feasible
+    histogram (one expert holding every spare row), is cut into ``n_bins``
+    equal-width bins, and the first ``per_bin`` distinct histograms (distinct
+    as sorted count lists) landing in each bin are kept. Returns dicts with
+    ``counts`` (int64 [E], in proposal order), ``imbalance``, ``alpha``, ``bin``.
+    """
+    if M % align or min_rows % align or E * min_rows > M:
+        raise ValueError("M and min_rows must be multiples of align, and E*min_rows <= M")
+    rng = np.random.default_rng(seed)
+    peak = np.full(E, min_rows, dtype=np.int64)
+    peak[0] = M - (E - 1) * min_rows
+    i_max = imbalance_index(peak)
+    width = i_max / n_bins
+    bins: list[list[dict]] = [[] for _ in range(n_bins)]
+    seen = set()
+    for _ in range(max_draws):
+        alpha = 10.0 ** rng.uniform(*log10_alpha)
+        p = rng.dirichlet(np.full(E, alpha))
+        counts = _counts_from_proposal(p, M, align, min_rows)
+        key = tuple(sorted(counts.tolist()))
+        if key in seen:
+            continue
+        ih = imbalance_index(counts)
+        b = min(int(ih / width), n_bins - 1) if width > 0 else 0
+        if len(bins[b]) >= per_bin:
+            continue
+        seen.add(key)
+        bins[b].append({"counts": counts, "imbalance": ih, "alpha": alpha, "bin": b})
+        if all(len(x) >= per_bin for x in bins):
+            break
+    else:
+        raise RuntimeError(f"only {[len(x) for x in bins]} histograms per bin after {max_draws} proposals")
+    return [h for x in bins for h in x]
+
+
+def expert_orders(E: int, n: int = 4, seed: int = 41) -> list[np.ndarray]:
+    """``n`` fixed permutations of the expert index: which expert id gets which count."""
+    rng = np.random.default_rng(seed)
+    return [rng.permutation(E) for _ in range(n)]
+
+
+def projection_inputs(M: int, K: int, N: int, E: int, seed: int, device="cpu", x_sigma: float = 1.0,
+                      w_sigma: float = 0.02):
+    """Activations A [M, K] and per-expert weights W [E, K, N] as bf16 torch tensors on ``device``.
+
+    Drawn with torch's generator for that device seeded with ``seed`` (normals
+    in float32, rounded to bf16), so multi-gigabyte operands never pass
+    through host memory. The same seed on another device type gives other values.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    a = torch.empty((M, K), dtype=torch.bfloat16, device=device)
+    w = torch.empty((E, K, N), dtype=torch.bfloat16, device=device)
+    # fill in row blocks so the float32 staging stays small
+    step = max(1, (1 << 26) // max(K, 1))
+    for lo in range(0, M, step):
+        hi = min(M, lo + step)
+        a[lo:hi] = (torch.randn((hi - lo, K), generator=g, device=device) * x_sigma).to(torch.bfloat16)
+    step = max(1, (1 << 26) // max(N, 1))
+    for e in range(E):
+        for lo in range(0, K, step):
+            hi = min(K, lo + step)
+            w[e, lo:hi] = (torch.randn((hi - lo, N), generator=g, device=device) * w_sigma).to(torch.bfloat16)
+    return a, w
