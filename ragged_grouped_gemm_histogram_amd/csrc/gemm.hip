@@ -132,6 +132,22 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_off(uint64_t base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// A pointer every lane holds the same value of, moved to SGPRs.
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -339,21 +355,25 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
     const TileCoord tc = tile_coord<C::BM, TILE_N>(t, n_tiles, total_mt, g.E, pl);
     const uint16_t* Wexp = g.W + (int64_t)tc.e * g.w_expert_stride;
 
-    // Source of each lane's 16-byte chunk for k0 = 0. A wave load fills 1 KB of
-    // LDS (lane l -> bytes [16l, 16l+16)), so the swizzle is applied by choosing
-    // which global chunk each lane fetches. Rows past the expert's block and
-    // columns past N are pointed at valid rows/columns: they only feed outputs
-    // that are never stored.
-    const uint16_t* a_src[C::A_OPS];
+    // Source of each lane's 16-byte chunk for k0 = 0, as a byte offset from a
+    // wave-uniform base (the host guarantees the offsets fit in 32 bits). A wave
+    // load fills 1 KB of LDS (lane l -> bytes [16l, 16l+16)), so the swizzle is
+    // applied by choosing which global chunk each lane fetches. Rows past the
+    // expert's block and columns past N are pointed at valid rows/columns: they
+    // only feed outputs that are never stored.
+    const uint64_t a_base = uniform_addr(g.a_rows != nullptr ? g.A : g.A + tc.row0 * g.lda);
+    uint32_t a_off[C::A_OPS];
 #pragma unroll
     for (int t2 = 0; t2 < C::A_OPS; ++t2) {
       const int j = wave + C::NWAVES * t2;
       const int r = 8 * j + (lane >> 3);
       const int c = swz(r, lane & 7);  // the swizzle is an involution: position -> logical chunk
       const int rr = r < tc.rows_valid ? r : tc.rows_valid - 1;
-      a_src[t2] = g.A + a_row_of(g, tc.row0 + rr) * g.lda + c * 8;
+      const int64_t arow = g.a_rows != nullptr ? a_row_of(g, tc.row0 + rr) : (int64_t)rr;
+      a_off[t2] = (uint32_t)((arow * g.lda + c * 8) * 2);
     }
-    const uint16_t* b_src[C::B_OPS];
+    const uint64_t b_base = uniform_addr(Wexp);
+    uint32_t b_off[C::B_OPS];
 #pragma unroll
     for (int t2 = 0; t2 < C::B_OPS; ++t2) {
       const int j = wave + C::NWAVES * t2;
@@ -371,7 +391,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
           if (n >= g.N) n = tc.n0;
           wrow = n;
         }
-        b_src[t2] = Wexp + wrow * g.ldw + c * 8;
+        b_off[t2] = (uint32_t)((wrow * g.ldw + c * 8) * 2);
       } else {
         // 64 k-rows of BN columns, chunk positions swizzled by swz_n
         constexpr int kRowsPerOp = 1024 / (BN * 2);
@@ -380,20 +400,22 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         const int c = swz_n(r, lane % kChunksRow);
         int64_t col = tc.n0 + c * 8;
         if (col >= g.N) col = tc.n0;
-        b_src[t2] = Wexp + (int64_t)r * g.ldw + col;
+        b_off[t2] = (uint32_t)(((int64_t)r * g.ldw + col) * 2);
       }
     }
+    const uint64_t b_step = (uint64_t)(B_NMAJOR ? BK * g.ldw : BK) * 2;
     auto issue = [&](int kt) {
       const uint32_t sa = lds0 + (uint32_t)((kt % NST) * C::STAGE_BYTES);
       const uint32_t sb = sa + C::A_BYTES;
-      const int64_t k0 = (int64_t)kt * BK;
+      const uint64_t ak = a_base + (uint64_t)kt * (BK * 2);
+      const uint64_t bk = b_base + (uint64_t)kt * b_step;
+      const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
 #pragma unroll
       for (int t2 = 0; t2 < C::A_OPS; ++t2)
-        dma16(a_src[t2] + k0, __builtin_amdgcn_readfirstlane(sa + (uint32_t)((wave + C::NWAVES * t2) * 1024)));
+        dma16_off(ak, a_off[t2], sa + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
 #pragma unroll
       for (int t2 = 0; t2 < C::B_OPS; ++t2)
-        dma16(B_NMAJOR ? b_src[t2] + k0 * g.ldw : b_src[t2] + k0,
-              __builtin_amdgcn_readfirstlane(sb + (uint32_t)((wave + C::NWAVES * t2) * 1024)));
+        dma16_off(bk, b_off[t2], sb + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
     };
 
     f32x16 acc[C::FM][C::FN];
@@ -636,7 +658,8 @@ hipError_t launch_kernel(Kern kern, bool* attr_done, const GemmArgs& g, hipStrea
 // 256 x 256 tiles on 8 waves (two per SIMD, so one wave's LDS and barrier waits
 // overlap the other's MFMAs) with a 2-stage ring; smaller blocks take 128 x 256
 // tiles on 8 waves with a 3-stage ring, which wastes fewer rows on ragged
-// tails. K not a multiple of 64 takes the register-staged loop.
+// tails. K not a multiple of 64, or operands too large for 32-bit load
+// offsets, take the register-staged loop.
 template <bool GATED>
 using BigTile = Tile<256, 256, 2, 4, 2, GATED>;
 template <bool GATED>
@@ -644,9 +667,18 @@ using SmallTile = Tile<128, 256, 2, 4, 3, GATED>;
 template <bool GATED>
 using RegsTile = Tile<128, 256, 2, 2, 2, GATED>;
 
+// The pipelined loop addresses its loads as 32-bit byte offsets from per-tile
+// bases: A rows of one tile (or, gathered, the whole token matrix) and one
+// expert's weights must each span less than 4 GiB.
+inline bool offsets_fit_32(const GemmArgs& g) {
+  constexpr int64_t kMax = 0xFFFFFFFFll;
+  const int64_t a_span = g.a_rows != nullptr ? g.a_tokens * g.lda * 2 : (int64_t)256 * g.lda * 2;
+  return a_span <= kMax && g.w_expert_stride * 2 <= kMax;
+}
+
 template <bool GATED, bool B_NMAJOR>
 hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
-  if (g.K % BK == 0) {
+  if (g.K % BK == 0 && offsets_fit_32(g)) {
     if (g.cap_rows >= (int64_t)384 * g.E) {
       static bool done[64] = {};
       return launch_kernel<BigTile<GATED>>(grouped_gemm_pipe_kernel<BigTile<GATED>, B_NMAJOR>, done, g, stream);
