@@ -148,13 +148,37 @@ __device__ __forceinline__ uint64_t uniform_addr(const void* p) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// vmcnt(N) together with lgkmcnt(0): this wave's own LDS reads are complete
+// too, whatever order the compiler left them in, before a barrier after which
+// other waves may overwrite the slot those reads came from.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vmcnt_lds() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
 }
 
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+// Barrier for LDS hand-offs only: this wave's LDS accesses are complete, its
+// global stores may still be in flight (a full __syncthreads would wait for
+// their write acknowledgements too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+// Scheduling hint for one K slice: spread READS LDS reads (the next slice's
+// fragments) between the MFMAS matrix instructions of the current one, so the
+// reads' latency hides behind matrix work instead of stalling the next slice.
+template <int MFMAS, int READS>
+__device__ __forceinline__ void interleave_reads() {
+  constexpr int kPer = MFMAS / READS > 0 ? MFMAS / READS : 1;
+  constexpr int kPairs = READS < MFMAS ? READS : MFMAS;
+#pragma unroll
+  for (int i = 0; i < kPairs; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+  }
+  if constexpr (MFMAS > kPairs * kPer) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - kPairs * kPer, 0);
+  if constexpr (READS > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, READS - kPairs, 0);
+}
 
 // Map a persistent workgroup to a logical worker so that consecutive logical
 // workers (which take consecutive tiles) sit on one XCD: workgroups are
@@ -245,7 +269,9 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int 
 }
 
 // Registers -> bf16 tile in LDS (swizzled 16-byte chunks) -> global. For the
-// gated projection, SwiGLU is applied here: g and u are rounded to bf16 first.
+// gated projection, SwiGLU is applied here: g and u are rounded to bf16 first,
+// then SiLU(g) * u is evaluated in fp32 with the hardware exponential and
+// reciprocal (a few fp32 ulps, far below the bf16 rounding of the result).
 // acc[i][j][4q+s] is output row (wm*WTM + i*32 + lane%32), column
 // (block column base + 8q + 4*(lane/32) + s).
 template <class C>
@@ -271,7 +297,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
           for (int s = 0; s < 4; ++s) {
             const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][4 * q + s]));
             const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + half_fn][4 * q + s]));
-            hv[s] = gv / (1.0f + __expf(-gv)) * uv;
+            hv[s] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           }
           const int col = wn * (BN / 2 / C::WGN) + j * 32 + 8 * q + 4 * half_lane;
           const int c = col >> 3;
@@ -297,7 +323,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   constexpr int kStoreIters = BM * C::OUT_CPR / C::THREADS;
 #pragma unroll
   for (int it = 0; it < kStoreIters; ++it) {
@@ -309,7 +335,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
       *reinterpret_cast<u32x4*>(g.out + (tc.row0 + r) * g.ldo + col) = v;
     }
   }
-  __syncthreads();  // LDS is reused by the next tile
+  lds_barrier();  // LDS is reused by the next tile
 }
 
 // weight-tile row of a wave's fn-th 32-row block (gated: the first FN/2 blocks are gate rows,
@@ -426,59 +452,95 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // Fragments of one 16-deep K slice: A rows of the wave tile and B columns.
+    // Two register sets: the slice the MFMAs consume and the next one, read
+    // from LDS while those MFMAs run.
+    bf16x8 af[2][C::FM], bfr[2][C::FN];
+    auto load_frags = [&](int set, int slot, int ks) {
+      const unsigned char* as = smem + slot * C::STAGE_BYTES;
+      const unsigned char* bs = as + C::A_BYTES;
+      const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int r = wm * C::WTM + i * 32 + (lane & 31);
+        af[set][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + r * (BK * 2) + swz(r, chunk) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (!B_NMAJOR) {
+          const int r = b_block_row<C>(wn, j) + (lane & 31);
+          bfr[set][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + r * (BK * 2) + swz(r, chunk) * 16));
+        } else {
+          // lane l gets k = 16ks + 8(l/32) + 0..7 of column nb0 + l%32: two transpose reads of
+          // 4 k each; in a 16-lane group lane j points at k-row j/4, columns 4(j%4)..+3.
+          const int nb0 = wn * C::WTN + j * 32;
+          const int c = (nb0 >> 3) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+          uint2 part[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int krow = ks * 16 + 8 * (lane >> 5) + 4 * q + ((lane & 15) >> 2);
+            const unsigned char* p = bs + krow * (BN * 2) + swz_n(krow, c) * 16 + (lane & 1) * 8;
+            const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(p));
+            part[q] = __builtin_bit_cast(uint2, v);
+          }
+          bfr[set][j] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
+        }
+      }
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+    };
+    // Stage kt is complete for this wave once only the later stages already
+    // issued are still in flight; after the barrier it is complete for every
+    // wave, and every wave has finished reading the stage before it.
+    auto wait_stage = [&](int kt) {
+      const int ahead = min(nk - 1, kt + NST - 2) - kt;  // stages issued after kt, still allowed in flight
+      if (NST >= 4 && ahead >= 2) wait_vmcnt_lds<(NST >= 4 ? 2 : 0) * OPS>();
+      else if (NST >= 3 && ahead >= 1) wait_vmcnt_lds<(NST >= 3 ? 1 : 0) * OPS>();
+      else wait_vmcnt_lds<0>();
+      bare_barrier();
+    };
+
+    // The next slice's fragments are read during the current slice's MFMAs when
+    // registers allow; the 256-row N-major tile has no room for the second set
+    // and reads each slice just before its MFMAs (the other wave on the SIMD
+    // covers the wait).
+    constexpr bool kPrefetch = !(B_NMAJOR && C::FM * C::FN >= 8);
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
       if (s < nk) issue(s);
+    wait_stage(0);
+    if constexpr (kPrefetch) load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      // Stage kt is complete for this wave once only the later stages already issued are
-      // in flight; after the barrier it is complete for every wave, and every wave has
-      // finished reading stage kt-1, whose slot the next issue overwrites.
-      const int ahead = min(nk, kt + NST - 1) - kt - 1;
-      if (NST >= 4 && ahead >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * OPS>();
-      else if (NST >= 3 && ahead >= 1) wait_vmcnt<(NST >= 3 ? 1 : 0) * OPS>();
-      else wait_vmcnt<0>();
-      bare_barrier();
+      // The slot stage kt+NST-1 fills held stage kt-1, which every wave finished
+      // reading before the barrier that made stage kt visible.
       if (kt + NST - 1 < nk) issue(kt + NST - 1);
-      const unsigned char* as = smem + (kt % NST) * C::STAGE_BYTES;
-      const unsigned char* bs = as + C::A_BYTES;
+      const int slot = kt % NST;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        const int chunk = 2 * ks + (lane >> 5);
-        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          const int r = wm * C::WTM + i * 32 + (lane & 31);
-          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + r * (BK * 2) + swz(r, chunk) * 16));
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          if constexpr (!B_NMAJOR) {
-            const int r = b_block_row<C>(wn, j) + (lane & 31);
-            bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + r * (BK * 2) + swz(r, chunk) * 16));
-          } else {
-            // lane l gets k = 16ks + 8(l/32) + 0..7 of column nb0 + l%32: two transpose reads of
-            // 4 k each; in a 16-lane group lane j points at k-row j/4, columns 4(j%4)..+3.
-            const int nb0 = wn * C::WTN + j * 32;
-            const int c = (nb0 >> 3) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-            uint2 part[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int krow = ks * 16 + 8 * (lane >> 5) + 4 * q + ((lane & 15) >> 2);
-              const unsigned char* p = bs + krow * (BN * 2) + swz_n(krow, c) * 16 + (lane & 1) * 8;
-              const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(p));
-              part[q] = __builtin_bit_cast(uint2, v);
-            }
-            bfr[j] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
+        const int cur = ks & 1;
+        if constexpr (!kPrefetch) {
+          load_frags(0, slot, ks);
+          mfmas(0);
+          if (ks + 1 == BK / 16 && kt + 1 < nk) wait_stage(kt + 1);
+        } else if (ks + 1 < BK / 16) {
+          load_frags(cur ^ 1, slot, ks + 1);
+          mfmas(cur);
+          interleave_reads<C::FM * C::FN, C::FM + (B_NMAJOR ? 2 : 1) * C::FN>();
+        } else {
+          mfmas(cur);
+          if (kt + 1 < nk) {
+            wait_stage(kt + 1);
+            load_frags(0, (kt + 1) % NST, 0);
           }
         }
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with the ring before the epilogue reuses it
+    lds_barrier();  // every wave is done with the ring (all its loads were waited for) before the epilogue reuses it
     epilogue<C>(acc, smem, g, tc);
   }
 }
