@@ -87,6 +87,10 @@ def _fuzz_cases():
         dict(T=900, k=2, E=3, d=320, h=192, seed=7, drop_frac=0.05),
         dict(T=200, k=3, E=4, d=320, h=192, seed=8, drop_frac=0.05, empty_experts=(2,)),
         dict(T=1100, k=1, E=2, d=576, h=448, seed=9, drop_frac=0.0),
+        # many tiles per workgroup with one or two K stages per tile: the load stream runs
+        # across tile boundaries (256-row tiles on the gate/up side, 128-row on the down side)
+        dict(T=20000, k=2, E=8, d=64, h=256, seed=10, drop_frac=0.02),
+        dict(T=6000, k=4, E=96, d=128, h=64, seed=11, drop_frac=0.1, empty_experts=(5, 50)),
     ]
     return cases
 

@@ -73,6 +73,25 @@ def test_projection_whole(counts, K, N):
     assert (bits(y)[M:] == bits(torch.tensor(3.0, dtype=torch.bfloat16))).all(), "rows past M were written"
 
 
+@pytest.mark.parametrize("counts,K,N", [
+    ([50000] * 4, 64, 512),               # 256-row tiles, one K stage each, ~6 tiles per workgroup
+    ([100] * 300 + [0] * 20 + [37] * 280, 64, 1024),  # 128-row tiles (3-slot ring), one K stage each
+    ([3000] * 7 + [5], 128, 256),         # two K stages per tile
+], ids=["big-k64", "small-k64", "big-k128"])
+def test_projection_stream_across_tiles(counts, K, N):
+    """Several tiles per workgroup with fewer K stages than ring slots: the loads of the next
+    tile's first stages overlap the current tile's last stage and epilogue."""
+    say(f"[gpu] projection stream E={len(counts)} M={sum(counts)} K={K} N={N}")
+    rng = np.random.default_rng(len(counts) + K)
+    M = sum(counts)
+    a = to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w = to_bf16_bits(0.1 * rng.standard_normal((len(counts), K, N), dtype=np.float32))
+    offs = _offsets(counts)
+    y = moe.moe_gemm_down(to_dev_bf16(a), to_dev(offs), to_dev_bf16(w))
+    torch.cuda.synchronize()
+    say("  " + str(compare_bf16(bits(y), oracle.grouped_projection(a, offs, w), "y")))
+
+
 @pytest.fixture(scope="module")
 def sweep_operands():
     E, M, dim = SWEEP["E"], SWEEP["M"], SWEEP["dim"]
