@@ -28,6 +28,7 @@ which the method states its accumulation; the test suite pins the two against
 each other within the float32 error bound.
 """
 
+from .backward import grouped_dgrad, grouped_wgrad, permute_backward, unpermute_backward
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
 from .moe import (
     MoeOracleResult,
@@ -57,6 +58,11 @@ __all__ = [
     "exclusive_offsets",
     "expert_forward",
     "f64_to_bf16_bits",
+    "grouped_dgrad",
+    "grouped_projection",
+    "grouped_wgrad",
+    "permute_backward",
+    "unpermute_backward",
     "moe_expert_forward",
     "padding_fraction",
     "permute_rows",

@@ -329,6 +329,87 @@ def pin_projection_is_down_step(orc) -> None:
     np.testing.assert_array_equal(y, r.y_perm)
 
 
+def _ragged_projection_case(seed, counts, d_in, d_out):
+    rng = np.random.default_rng(seed)
+    M = sum(counts)
+    x = to_bf16_bits(rng.standard_normal((M, d_in), dtype=np.float32))
+    dy = to_bf16_bits(rng.standard_normal((M, d_out), dtype=np.float32))
+    w = to_bf16_bits(0.2 * rng.standard_normal((len(counts), d_in, d_out), dtype=np.float32))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return x, dy, w, offsets
+
+
+def pin_backward_is_autograd(orc) -> None:
+    """Eq 15 through torch autograd: a per-expert loop Y_e = X_e W_e (and Y_e = X_e W_e^T for the
+    [E, d_out, d_in] layout) in float64, differentiated by autograd against a fixed dY, gives the
+    oracle's Dgrad and Wgrad (torch bf16 rounding of autograd's float64 sums)."""
+    counts = [5, 0, 9, 1, 3]
+    d_in, d_out = 12, 20  # d_in != d_out: a missing transpose cannot type-check
+    x, dy, w, offsets = _ragged_projection_case(71, counts, d_in, d_out)
+    for layout in ("in_out", "out_in"):
+        w_l = w if layout == "in_out" else np.ascontiguousarray(np.swapaxes(w, 1, 2))
+        xt = _bits_to_f64(x).requires_grad_(True)
+        wt = _bits_to_f64(w_l).requires_grad_(True)
+        ys = []
+        for e in range(len(counts)):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            we = wt[e] if layout == "in_out" else wt[e].T
+            ys.append(xt[lo:hi] @ we)
+        y = torch.cat(ys)
+        (y * _bits_to_f64(dy)).sum().backward()
+        _assert_close_bits(orc.grouped_dgrad(dy, offsets, w_l, layout), _torch_bf16_bits(xt.grad.detach()),
+                           f"Dgrad {layout}", min_exact=0.999, max_ulp=1)
+        _assert_close_bits(orc.grouped_wgrad(x, dy, offsets, layout), _torch_bf16_bits(wt.grad.detach()),
+                           f"Wgrad {layout}", min_exact=0.999, max_ulp=1)
+
+
+def pin_backward_brute_force(orc) -> None:
+    """Pure-Python loops over every element of Dgrad and Wgrad on a ragged case with an empty expert."""
+    counts = [2, 0, 3]
+    d_in, d_out = 4, 5
+    x, dy, w, offsets = _ragged_projection_case(73, counts, d_in, d_out)
+    xv, gv, wv = _bits_to_f64(x).tolist(), _bits_to_f64(dy).tolist(), _bits_to_f64(w).tolist()
+    ref_dx = np.zeros((sum(counts), d_in), dtype=np.uint16)
+    ref_dw = np.zeros((len(counts), d_in, d_out), dtype=np.uint16)
+    for e in range(len(counts)):
+        rows = range(int(offsets[e]), int(offsets[e + 1]))
+        for r in rows:
+            ref_dx[r] = _torch_bf16_bits(torch.tensor([sum(gv[r][o] * wv[e][i][o] for o in range(d_out))
+                                                       for i in range(d_in)], dtype=torch.float64))
+        for i in range(d_in):
+            ref_dw[e, i] = _torch_bf16_bits(torch.tensor([sum(xv[r][i] * gv[r][o] for r in rows)
+                                                          for o in range(d_out)], dtype=torch.float64))
+    _assert_close_bits(orc.grouped_dgrad(dy, offsets, w), ref_dx, "Dgrad brute force", min_exact=1.0, max_ulp=0)
+    _assert_close_bits(orc.grouped_wgrad(x, dy, offsets), ref_dw, "Wgrad brute force", min_exact=1.0, max_ulp=0)
+
+
+def pin_permutation_backward_is_autograd(orc) -> None:
+    """The two permutations' backward through torch autograd: the row gather X[perm/k] (whose
+    autograd backward is a scatter-add) and the weighted gather-sum of the unpermute."""
+    wl = make_random(T=25, k=3, E=4, d=16, h=8, seed=81, drop_frac=0.2)
+    r = orc.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, with_gemm=False)
+    M, T, k = r.M, wl.T, wl.k
+    rng = np.random.default_rng(82)
+    g_perm = to_bf16_bits(rng.standard_normal((M, wl.d), dtype=np.float32))
+    xt = _bits_to_f64(wl.x).requires_grad_(True)
+    xp = xt[torch.from_numpy(r.perm[:M].astype(np.int64) // k)]
+    (xp * _bits_to_f64(g_perm)).sum().backward()
+    _assert_close_bits(orc.permute_backward(g_perm, r.inv_map, T, k), _torch_bf16_bits(xt.grad.detach()),
+                       "permute backward", min_exact=0.999, max_ulp=1)
+    y_perm = to_bf16_bits(rng.standard_normal((M, wl.d), dtype=np.float32))
+    dy = to_bf16_bits(rng.standard_normal((T, wl.d), dtype=np.float32))
+    ypt = _bits_to_f64(y_perm).requires_grad_(True)
+    wt = torch.from_numpy(wl.routing_w.astype(np.float64)).requires_grad_(True)
+    inv = torch.from_numpy(r.inv_map.astype(np.int64))
+    keep = (inv >= 0).double()
+    gathered = ypt[inv.clamp(min=0)] * keep[..., None]  # [T, k, d]
+    y = (wt[..., None] * gathered).sum(1)
+    (y * _bits_to_f64(dy)).sum().backward()
+    dyp, dw = orc.unpermute_backward(dy, y_perm, r.inv_map, wl.routing_w, T, k, M)
+    _assert_close_bits(dyp, _torch_bf16_bits(ypt.grad.detach()), "unpermute backward rows", min_exact=1.0, max_ulp=0)
+    np.testing.assert_allclose(dw, wt.grad.detach().numpy().astype(np.float32), rtol=1e-6, atol=1e-6)
+
+
 ALL_PINS = [
     pin_toy_golden,
     pin_printed_arithmetic,
@@ -343,4 +424,7 @@ ALL_PINS = [
     pin_projection_column_partition,
     pin_projection_brute_force,
     pin_projection_is_down_step,
+    pin_backward_is_autograd,
+    pin_backward_brute_force,
+    pin_permutation_backward_is_autograd,
 ]

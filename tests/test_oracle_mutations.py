@@ -103,6 +103,46 @@ def _projection_unrounded(a_bits, offsets, w_bits, precision="f64"):
     return out
 
 
+import oracle.backward as ob
+
+_orig_dgrad = ob.grouped_dgrad
+_orig_wgrad = ob.grouped_wgrad
+_orig_permute_bwd = ob.permute_backward
+_orig_unpermute_bwd = ob.unpermute_backward
+
+
+def _dgrad_no_transpose(dy_bits, offsets, w_bits, layout="in_out", precision="f64"):
+    # the layout flag ignored: every weight read as [d_in, d_out]
+    return _orig_dgrad(dy_bits, offsets, w_bits, "in_out", precision)
+
+
+def _wgrad_shifted(x_bits, dy_bits, offsets, layout="in_out", precision="f64"):
+    # each expert's gradient written to the next expert's slot
+    return np.roll(_orig_wgrad(x_bits, dy_bits, offsets, layout, precision), 1, axis=0)
+
+
+def _wgrad_rows_off_by_one(x_bits, dy_bits, offsets, layout="in_out", precision="f64"):
+    # the contraction stops one row short of each expert's block
+    offs = np.asarray(offsets).astype(np.int64)
+    out = _orig_wgrad(x_bits, dy_bits, offs, layout, precision)
+    for e in range(offs.shape[0] - 1):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi - lo >= 1:
+            sub = np.array([0, hi - lo - 1], dtype=np.int64)
+            out[e] = _orig_wgrad(np.asarray(x_bits)[lo:hi], np.asarray(dy_bits)[lo:hi], sub, layout, precision)[0]
+    return out
+
+
+def _permute_bwd_first_slot_only(dx_perm_bits, inv, T, k, precision="f64"):
+    inv = np.asarray(inv).reshape(T, k).copy()
+    inv[:, 1:] = -1
+    return _orig_permute_bwd(dx_perm_bits, inv, T, k, precision)
+
+
+def _unpermute_bwd_unweighted(dy_bits, y_perm_bits, inv, routing_w, T, k, M):
+    return _orig_unpermute_bwd(dy_bits, y_perm_bits, inv, np.ones_like(np.asarray(routing_w)), T, k, M)
+
+
 MUTATIONS = {
     "silu_sign": [("_swiglu_expert", _swiglu_variant(silu_sign=-1.0))],
     "gate_up_swapped": [("_swiglu_expert", _swiglu_variant(gate_up_swapped=True))],
@@ -118,13 +158,18 @@ MUTATIONS = {
     "projection_wrong_expert": [("grouped_projection", _projection_shifted)],
     "projection_rows_shifted": [("grouped_projection", _projection_rows_shifted)],
     "projection_truncated": [("grouped_projection", _projection_unrounded)],
+    "dgrad_layout_ignored": [("grouped_dgrad", _dgrad_no_transpose)],
+    "wgrad_wrong_expert": [("grouped_wgrad", _wgrad_shifted)],
+    "wgrad_row_short": [("grouped_wgrad", _wgrad_rows_off_by_one)],
+    "permute_backward_one_slot": [("permute_backward", _permute_bwd_first_slot_only)],
+    "unpermute_backward_unweighted": [("unpermute_backward", _unpermute_bwd_unweighted)],
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     for attr, fn in MUTATIONS[name]:
-        monkeypatch.setattr(om, attr, fn)
+        monkeypatch.setattr(ob if hasattr(ob, attr) and not hasattr(om, attr) else om, attr, fn)
         if hasattr(oracle, attr):
             monkeypatch.setattr(oracle, attr, fn)
     caught = []
