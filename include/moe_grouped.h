@@ -176,6 +176,72 @@ moe_status moe_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const ui
 moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const float* routing_w, int64_t T,
                          int32_t k, int64_t d, uint16_t* y, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward (OLMo report Sec 9.5, Eq 15 and Table 15; halo notes on the
+ * atomic-free permute backward). For one grouped projection Y_e = X_e W_e with
+ * X_e [M_e, d_in] and W_e [d_in, d_out], Dgrad dX_e = dY_e W_e^T keeps M_e as
+ * its output rows and Wgrad dW_e = X_e^T dY_e contracts over M_e. Weights are
+ * stored in one of two layouts:
+ *   MOE_W_IN_OUT  [E, d_in, d_out]  (W_down [E, h, d]: d_in = h, d_out = d)
+ *   MOE_W_OUT_IN  [E, d_out, d_in]  (W_ug [E, 2h, d]: d_in = d, d_out = 2h)
+ * bf16 inputs, fp32 accumulation, bf16 outputs (round-to-nearest-even).
+ * Offsets are clamped as in the forward.
+ * ------------------------------------------------------------------------- */
+typedef enum moe_weight_layout { MOE_W_IN_OUT = 0, MOE_W_OUT_IN = 1 } moe_weight_layout;
+
+/* Dgrad: dx[rows_e] = bf16(dy[rows_e] * W_e^T) for every expert e.
+ *
+ *   dy       bf16  [cap_rows, d_out]
+ *   offsets  int32 [E+1]
+ *   w        bf16  [E, d_in, d_out] or [E, d_out, d_in] per w_layout
+ *   dx       bf16  [cap_rows, d_in] out (rows past M untouched)
+ *
+ * A forward-shaped grouped GEMM (K = d_out, N = d_in): same kernels and tile
+ * choice as the forward projections. An unknown w_layout is MOE_ERR_BAD_SHAPE. */
+moe_status moe_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, int32_t w_layout,
+                             int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
+                             hipStream_t stream);
+
+/* Wgrad: dW_e = bf16(x[rows_e]^T * dy[rows_e]), written [E, d_in, d_out]
+ * (MOE_W_IN_OUT) or transposed [E, d_out, d_in] (MOE_W_OUT_IN), so the
+ * gradient has the layout of the weight it belongs to.
+ *
+ *   x        bf16  [cap_rows, d_in]    the projection's input rows
+ *   dy       bf16  [cap_rows, d_out]   the gradient of its output rows
+ *   offsets  int32 [E+1]
+ *   dw       bf16  [E * d_in * d_out]  out, every element written; an expert
+ *                                     with no rows gets zeros
+ *
+ * One persistent launch over 256 x 256 output tiles, largest experts first. */
+moe_status moe_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, int32_t w_layout,
+                             int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
+                             hipStream_t stream);
+
+/* Backward of moe_permute's row gather (x_perm[p] = x[perm[p] / k]):
+ * dx[t] = bf16(sum over kept j, ascending, of dx_perm[inv_map[t, j]]), fp32
+ * accumulation; a gather through the inverse map, no atomics.
+ *
+ *   dx_perm  bf16  [T*k, d]
+ *   inv_map  int32 [T, k]   entries outside [0, T*k) are skipped
+ *   dx       bf16  [T, d]   out, every row written (zeros for a token with no
+ *                           kept slot) */
+moe_status moe_permute_backward(const uint16_t* dx_perm, const int32_t* inv_map, int64_t T, int32_t k, int64_t d,
+                                uint16_t* dx, hipStream_t stream);
+
+/* Backward of moe_unpermute (y[t] = sum_j w[t, j] * y_perm[inv_map[t, j]]):
+ *
+ *   dy           bf16  [T, d]
+ *   y_perm       bf16  [T*k, d]  the forward's expert outputs
+ *   inv_map      int32 [T, k]
+ *   routing_w    fp32  [T, k]
+ *   dy_perm      bf16  [T*k, d]  out: row inv_map[t, j] = bf16(w[t, j] * dy[t])
+ *                                for kept slots; other rows untouched
+ *   d_routing_w  fp32  [T, k]    out: sum_c dy[t, c] * y_perm[inv_map[t, j], c]
+ *                                (fp32), 0 for dropped slots */
+moe_status moe_unpermute_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* inv_map,
+                                  const float* routing_w, int64_t T, int32_t k, int64_t d, uint16_t* dy_perm,
+                                  float* d_routing_w, hipStream_t stream);
+
 /* A static, human-readable name for a status code. */
 const char* moe_status_string(moe_status s);
 

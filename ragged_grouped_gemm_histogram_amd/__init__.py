@@ -36,8 +36,14 @@ _SIGNATURES = {
     "grouped_swiglu_expert_gather": (ctypes.c_int,
                                      [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_unpermute": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
+    "moe_grouped_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_grouped_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_permute_backward": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _vp, _vp]),
+    "moe_unpermute_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
+
+W_LAYOUTS = {"in_out": 0, "out_in": 1}  # [E, d_in, d_out] / [E, d_out, d_in]
 
 
 _LIB = None
@@ -259,6 +265,87 @@ def moe_unpermute(y_perm: torch.Tensor, inv_map: torch.Tensor, routing_w: torch.
     return y
 
 
+def _w_dims(w: torch.Tensor, layout: str):
+    if layout not in W_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(W_LAYOUTS)}, got {layout!r}")
+    if w.dim() != 3:
+        raise ValueError("expert weights must be 3-D")
+    E, a, b = w.shape
+    return (E, a, b) if layout == "in_out" else (E, b, a)  # E, d_in, d_out
+
+
+def moe_grouped_dgrad(dy: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor, layout: str = "in_out", *,
+                      dx=None) -> torch.Tensor:
+    """dX[rows_e] = bf16(dY[rows_e] @ W_e^T) for the projection Y_e = X_e W_e (one launch)."""
+    E, d_in, d_out = _w_dims(w, layout)
+    if dy.dim() != 2:
+        raise ValueError("dy must be [cap_rows, d_out]")
+    cap, dev = dy.shape[0], dy.device
+    _want(dy, "dy", torch.bfloat16, (cap, d_out), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w, "w", torch.bfloat16, tuple(w.shape), dev)
+    dx = _out(dx, "dx", torch.bfloat16, (cap, d_in), dev)
+    _check(load_library().moe_grouped_dgrad(_ptr(dy), _ptr(offsets), _ptr(w), W_LAYOUTS[layout], cap, d_in, d_out, E,
+                                            _ptr(dx), _stream(dy)), "moe_grouped_dgrad")
+    return dx
+
+
+def moe_grouped_wgrad(x: torch.Tensor, dy: torch.Tensor, offsets: torch.Tensor, layout: str = "in_out", *,
+                      dw=None) -> torch.Tensor:
+    """dW_e = bf16(X[rows_e]^T @ dY[rows_e]) in the weight's layout; zeros for experts with no rows (one launch)."""
+    if x.dim() != 2 or dy.dim() != 2 or offsets.dim() != 1:
+        raise ValueError("expected x [cap, d_in], dy [cap, d_out] and offsets [E+1]")
+    cap, d_in = x.shape
+    d_out = dy.shape[1]
+    E = offsets.shape[0] - 1
+    dev = x.device
+    _want(x, "x", torch.bfloat16, (cap, d_in), dev)
+    _want(dy, "dy", torch.bfloat16, (cap, d_out), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    shape = (E, d_in, d_out) if layout == "in_out" else (E, d_out, d_in)
+    if layout not in W_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(W_LAYOUTS)}, got {layout!r}")
+    dw = _out(dw, "dw", torch.bfloat16, shape, dev)
+    _check(load_library().moe_grouped_wgrad(_ptr(x), _ptr(dy), _ptr(offsets), W_LAYOUTS[layout], cap, d_in, d_out, E,
+                                            _ptr(dw), _stream(x)), "moe_grouped_wgrad")
+    return dw
+
+
+def moe_permute_backward(dx_perm: torch.Tensor, inv_map: torch.Tensor, *, dx=None) -> torch.Tensor:
+    """dX[t] = bf16(sum over kept j of dx_perm[inv_map[t, j]]) (gather + reduce, no atomics)."""
+    if inv_map.dim() != 2:
+        raise ValueError("inv_map must be [T, k]")
+    T, k = inv_map.shape
+    dev = dx_perm.device
+    d = dx_perm.shape[1]
+    _want(dx_perm, "dx_perm", torch.bfloat16, (T * k, d), dev)
+    _want(inv_map, "inv_map", torch.int32, (T, k), dev)
+    dx = _out(dx, "dx", torch.bfloat16, (T, d), dev)
+    _check(load_library().moe_permute_backward(_ptr(dx_perm), _ptr(inv_map), T, k, d, _ptr(dx), _stream(dx_perm)),
+           "moe_permute_backward")
+    return dx
+
+
+def moe_unpermute_backward(dy: torch.Tensor, y_perm: torch.Tensor, inv_map: torch.Tensor, routing_w: torch.Tensor, *,
+                           dy_perm=None, d_routing_w=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Backward of moe_unpermute: (dy_perm with rows inv_map[t, j] = bf16(w[t, j] * dy[t]), d_routing_w fp32)."""
+    if inv_map.dim() != 2:
+        raise ValueError("inv_map must be [T, k]")
+    T, k = inv_map.shape
+    dev = dy.device
+    d = dy.shape[1]
+    _want(dy, "dy", torch.bfloat16, (T, d), dev)
+    _want(y_perm, "y_perm", torch.bfloat16, (T * k, d), dev)
+    _want(inv_map, "inv_map", torch.int32, (T, k), dev)
+    _want(routing_w, "routing_w", torch.float32, (T, k), dev)
+    dy_perm = _out(dy_perm, "dy_perm", torch.bfloat16, (T * k, d), dev)
+    d_routing_w = _out(d_routing_w, "d_routing_w", torch.float32, (T, k), dev)
+    _check(load_library().moe_unpermute_backward(_ptr(dy), _ptr(y_perm), _ptr(inv_map), _ptr(routing_w), T, k, d,
+                                                 _ptr(dy_perm), _ptr(d_routing_w), _stream(dy)),
+           "moe_unpermute_backward")
+    return dy_perm, d_routing_w
+
+
 def moe_expert_forward(x, expert_ids, routing_w, w_ug, w_down, fused_gather: bool = False):
     """The whole step: permute, grouped SwiGLU expert, unpermute. Returns (y, Permuted, h_buf, y_perm).
 
@@ -277,5 +364,6 @@ __all__ = [
     "LIB_PATH", "MAX_EXPERTS", "MoeError", "Permuted", "grouped_swiglu_expert", "header_functions", "load_library",
     "grouped_swiglu_expert_gather", "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu",
     "moe_gemm_up_swiglu_gather", "moe_permute", "moe_unpermute",
-    "permute_workspace_bytes",
+    "permute_workspace_bytes", "W_LAYOUTS", "moe_grouped_dgrad", "moe_grouped_wgrad", "moe_permute_backward",
+    "moe_unpermute_backward",
 ]

@@ -174,6 +174,68 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const f
   return launched(launch_unpermute(y_perm, inv_map, routing_w, T, k, d, y, stream));
 }
 
+moe_status moe_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, int32_t w_layout,
+                             int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
+                             hipStream_t stream) {
+  if (w_layout != MOE_W_IN_OUT && w_layout != MOE_W_OUT_IN) return MOE_ERR_BAD_SHAPE;
+  moe_status st = check_gemm_shape(cap_rows, d_in, d_out, E);
+  if (st != MOE_OK) return st;
+  if (missing(dy, cap_rows * d_out) || missing(offsets, E + 1) || missing(w, (int64_t)E * d_in * d_out) ||
+      missing(dx, cap_rows * d_in))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(dy, 16) || misaligned(w, 16) || misaligned(dx, 16) || misaligned(offsets, 4)) return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_grouped_dgrad(dy, offsets, w, w_layout == MOE_W_OUT_IN, cap_rows, d_in, d_out, E, dx, stream));
+}
+
+moe_status moe_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, int32_t w_layout,
+                             int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
+                             hipStream_t stream) {
+  if (w_layout != MOE_W_IN_OUT && w_layout != MOE_W_OUT_IN) return MOE_ERR_BAD_SHAPE;
+  moe_status st = check_gemm_shape(cap_rows, d_in, d_out, E);
+  if (st != MOE_OK) return st;
+  if (missing(x, cap_rows * d_in) || missing(dy, cap_rows * d_out) || missing(offsets, E + 1) ||
+      missing(dw, (int64_t)E * d_in * d_out))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x, 16) || misaligned(dy, 16) || misaligned(dw, 16) || misaligned(offsets, 4)) return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return launched(launch_grouped_wgrad(x, dy, offsets, w_layout == MOE_W_OUT_IN, cap_rows, d_in, d_out, E, dw, stream));
+}
+
+moe_status moe_permute_backward(const uint16_t* dx_perm, const int32_t* inv_map, int64_t T, int32_t k, int64_t d,
+                                uint16_t* dx, hipStream_t stream) {
+  if (T < 0 || k < 1 || bad_width(d) || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  if (missing(dx_perm, S * d) || missing(inv_map, S) || missing(dx, T * d)) return MOE_ERR_NULL_POINTER;
+  if (misaligned(dx_perm, 16) || misaligned(dx, 16) || misaligned(inv_map, 4)) return MOE_ERR_MISALIGNED;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_unpermute(dx_perm, inv_map, nullptr, T, k, d, dx, stream));
+}
+
+moe_status moe_unpermute_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* inv_map,
+                                  const float* routing_w, int64_t T, int32_t k, int64_t d, uint16_t* dy_perm,
+                                  float* d_routing_w, hipStream_t stream) {
+  if (T < 0 || k < 1 || bad_width(d) || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  if (missing(dy, T * d) || missing(y_perm, S * d) || missing(inv_map, S) || missing(routing_w, S) ||
+      missing(dy_perm, S * d) || missing(d_routing_w, S))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(dy, 16) || misaligned(y_perm, 16) || misaligned(dy_perm, 16) || misaligned(inv_map, 4) ||
+      misaligned(routing_w, 4) || misaligned(d_routing_w, 4))
+    return MOE_ERR_MISALIGNED;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_unpermute_backward(dy, y_perm, inv_map, routing_w, T, k, d, dy_perm, d_routing_w, stream));
+}
+
 const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";

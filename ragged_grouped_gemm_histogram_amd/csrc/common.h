@@ -57,10 +57,19 @@ hipError_t launch_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, 
                                         const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
                                         uint16_t* h_buf, hipStream_t stream);
 
+hipError_t launch_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, bool w_out_in,
+                                int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
+                                hipStream_t stream);
+hipError_t launch_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, bool w_out_in,
+                                int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
+                                hipStream_t stream);
 hipError_t launch_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down,
                             int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* y_perm,
                             hipStream_t stream);
 
+hipError_t launch_unpermute_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* inv, const float* w,
+                                     int64_t T, int32_t k, int64_t d, uint16_t* dy_perm, float* dw,
+                                     hipStream_t stream);
 hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* inv, const float* w, int64_t T, int32_t k,
                             int64_t d, uint16_t* y, hipStream_t stream);
 

@@ -43,7 +43,6 @@ namespace {
 constexpr int BK = 64;         // K per stage: 8 chunks of 16 bytes per tile row
 constexpr int kChunksK = BK / 8;
 constexpr int kGroupM = 8;     // m-tiles per group in the tile order (operand reuse in L2)
-constexpr int kStages = 3;     // LDS ring depth of the pipelined loop
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -124,15 +123,9 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(a, b, 0x05040100u); }
 __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(a, b, 0x07060302u); }
 
-// One 16-byte chunk per lane from `src` into LDS[lds_addr + 16 * lane] (M0 holds the wave's LDS base).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-// The same with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset.
+// One 16-byte chunk per lane from base + off (bytes) into LDS[lds_addr + 16 * lane]: a
+// wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset (M0 holds the
+// wave's LDS base).
 __device__ __forceinline__ void dma16_off(uint64_t base, uint32_t off, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -473,14 +466,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         } else {
           // lane l gets k = 16ks + 8(l/32) + 0..7 of column nb0 + l%32: two transpose reads of
           // 4 k each; in a 16-lane group lane j points at k-row j/4, columns 4(j%4)..+3.
+          // the swizzle depends on the k-row only through krow % 4, which ks and q
+          // leave unchanged: one lane address plus a constant slice offset
           const int nb0 = wn * C::WTN + j * 32;
           const int c = (nb0 >> 3) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+          const int kr = 8 * (lane >> 5) + ((lane & 15) >> 2);
+          const unsigned char* lane_p = bs + kr * (BN * 2) + swz_n(kr, c) * 16 + (lane & 1) * 8;
           uint2 part[2];
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const int krow = ks * 16 + 8 * (lane >> 5) + 4 * q + ((lane & 15) >> 2);
-            const unsigned char* p = bs + krow * (BN * 2) + swz_n(krow, c) * 16 + (lane & 1) * 8;
-            const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(p));
+            const v4i16 v =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(lane_p + (ks * 16 + 4 * q) * (BN * 2)));
             part[q] = __builtin_bit_cast(uint2, v);
           }
           bfr[set][j] = __builtin_bit_cast(bf16x8, u32x4{part[0].x, part[0].y, part[1].x, part[1].y});
@@ -506,10 +502,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
     };
 
     // The next slice's fragments are read during the current slice's MFMAs when
-    // registers allow; the 256-row N-major tile has no room for the second set
-    // and reads each slice just before its MFMAs (the other wave on the SIMD
-    // covers the wait).
-    constexpr bool kPrefetch = !(B_NMAJOR && C::FM * C::FN >= 8);
+    // registers allow; the 256x256 tiles with a plain (256-column) output have
+    // no room for the second set and read each slice just before its MFMAs
+    // (the other wave on the SIMD covers the wait).
+    constexpr bool kPrefetch = !((B_NMAJOR || !C::GATED) && C::FM * C::FN >= 8);
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
       if (s < nk) issue(s);
@@ -702,6 +698,193 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs 
   }
 }
 
+// ============================================================================
+// Wgrad: out[e] = A_e^T B_e, contracting over each expert's rows (Eq 15).
+// A [cap_rows, P] and B [cap_rows, Q] are both row-major, so a K stage (64 of
+// the expert's rows) lands in LDS row-contiguous for both operands and both
+// MFMA fragments come from transpose reads, as the N-major weights of the
+// forward do. The ragged contraction length is handled by clamping the rows a
+// tail stage loads to the expert's last row and zeroing A's fragment entries
+// past the block, so every product with a padded row is an exact zero.
+// ============================================================================
+struct WgradArgs {
+  const uint16_t* A;  // [cap_rows, P]
+  int64_t lda;
+  const uint16_t* B;  // [cap_rows, Q]
+  int64_t ldb;
+  int64_t P, Q;       // out[e] is [P, Q]
+  const int32_t* offsets;
+  int32_t E;
+  int64_t cap_rows;
+  uint16_t* out;      // [E, P, Q]
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_wgrad_kernel(WgradArgs g) {
+  constexpr int BM = C::BM, BN = C::BN, NST = C::NST;
+  static_assert(!C::GATED && NST == 2, "plain output, double-buffered ring");
+  static_assert(BM * 2 <= 1024 && BN * 2 <= 1024, "a stage row must fit one wave load");
+  constexpr int OPS = C::A_OPS + C::B_OPS;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int s_lo[MOE_MAX_EXPERTS], s_rows[MOE_MAX_EXPERTS], s_order[MOE_MAX_EXPERTS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+
+  // Clamped row block of every expert, then the experts in descending row
+  // count (ties by index): dealing the largest contractions first keeps the
+  // static round-robin schedule balanced.
+  for (int e = tid; e < g.E; e += C::THREADS) {
+    int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
+    lo = lo < 0 ? 0 : (lo > g.cap_rows ? g.cap_rows : lo);
+    hi = hi < lo ? lo : (hi > g.cap_rows ? g.cap_rows : hi);
+    s_lo[e] = (int)lo;
+    s_rows[e] = (int)(hi - lo);
+  }
+  __syncthreads();
+  for (int e = tid; e < g.E; e += C::THREADS) {
+    const int re = s_rows[e];
+    int rank = 0;
+    for (int f = 0; f < g.E; ++f) {
+      const int rf = s_rows[f];
+      rank += (rf > re || (rf == re && f < e)) ? 1 : 0;
+    }
+    s_order[rank] = e;
+  }
+  __syncthreads();
+
+  const int64_t m_tiles = (g.P + BM - 1) / BM, n_tiles = (g.Q + BN - 1) / BN;
+  const int64_t per_expert = m_tiles * n_tiles;
+  const int64_t total_tiles = per_expert * g.E;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const GemmArgs ge{nullptr, 0, nullptr, 1, 0, nullptr, 0, 0, 0, g.Q, 0, nullptr, g.E, 0, g.out, g.Q};
+
+  for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
+    const int pos = (int)(t / per_expert);
+    const int64_t rem = t - (int64_t)pos * per_expert;
+    const int e = __builtin_amdgcn_readfirstlane(s_order[pos]);
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e]);
+    const int rows = __builtin_amdgcn_readfirstlane(s_rows[e]);
+    const int64_t m0 = (rem / n_tiles) * BM, n0 = (rem % n_tiles) * BN;
+    const int nk = (rows + BK - 1) / BK;
+
+    // Per lane and wave load: stage row r (of 64) and the column chunk it fetches.
+    constexpr int kRowsA = 1024 / (BM * 2), kChunksA = BM / 8;
+    constexpr int kRowsB = 1024 / (BN * 2), kChunksB = BN / 8;
+    int a_r[C::A_OPS], b_r[C::B_OPS];
+    int a_col[C::A_OPS], b_col[C::B_OPS];  // P, Q < 2^24
+#pragma unroll
+    for (int t2 = 0; t2 < C::A_OPS; ++t2) {
+      const int j = wave + C::NWAVES * t2;
+      a_r[t2] = j * kRowsA + lane / kChunksA;
+      const int64_t col = m0 + swz_n(a_r[t2], lane % kChunksA) * 8;
+      a_col[t2] = (int)(col < g.P ? col : m0);
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < C::B_OPS; ++t2) {
+      const int j = wave + C::NWAVES * t2;
+      b_r[t2] = j * kRowsB + lane / kChunksB;
+      const int64_t col = n0 + swz_n(b_r[t2], lane % kChunksB) * 8;
+      b_col[t2] = (int)(col < g.Q ? col : n0);
+    }
+    auto issue = [&](int kt) {
+      const uint32_t sa = lds0 + (uint32_t)((kt % NST) * C::STAGE_BYTES);
+      const uint32_t sb = sa + C::A_BYTES;
+      const int row0 = lo + kt * BK;
+      const int left = rows - kt * BK;  // rows of this stage inside the block (>= 1)
+      const uint64_t ab = uniform_addr(g.A + (int64_t)row0 * g.lda);
+      const uint64_t bb = uniform_addr(g.B + (int64_t)row0 * g.ldb);
+      const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
+#pragma unroll
+      for (int t2 = 0; t2 < C::A_OPS; ++t2) {
+        const int r = a_r[t2] < left ? a_r[t2] : left - 1;
+        dma16_off(ab, (uint32_t)(((int64_t)r * g.lda + a_col[t2]) * 2), sa + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < C::B_OPS; ++t2) {
+        const int r = b_r[t2] < left ? b_r[t2] : left - 1;
+        dma16_off(bb, (uint32_t)(((int64_t)r * g.ldb + b_col[t2]) * 2), sb + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
+      }
+    };
+    // lane l gets k = 16ks + 8(l/32) + 0..7 of column cb + l%32 from a row-contiguous stage
+    // region whose rows are ROWB bytes: two transpose reads of four k each.
+    // The swizzle depends on the row only through row % 4, which ks and q leave
+    // unchanged, so the slice offset is a constant added to one lane address.
+    auto tr_frag = [&](const unsigned char* base, int rowb, int cb, int ks) {
+      const int c = (cb >> 3) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      const int kr = 8 * (lane >> 5) + ((lane & 15) >> 2);
+      const unsigned char* lane_p = base + kr * rowb + swz_n(kr, c) * 16 + (lane & 1) * 8;
+      uint2 part[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(lane_p + (ks * 16 + 4 * q) * rowb));
+        part[q] = __builtin_bit_cast(uint2, v);
+      }
+      return u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+    };
+
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    if (nk > 0) {
+      issue(0);
+      wait_vmcnt_lds<0>();
+      bare_barrier();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) issue(kt + 1);
+      const unsigned char* as = smem + (kt % NST) * C::STAGE_BYTES;
+      const unsigned char* bs = as + C::A_BYTES;
+      const int left = rows - kt * BK;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          u32x4 v = tr_frag(as, BM * 2, wm * C::WTM + i * 32, ks);
+          if (left < BK) {  // tail stage: zero A entries of rows past the block
+            const int k0 = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t keep_lo = k0 + 2 * w < left ? 0x0000FFFFu : 0u;
+              const uint32_t keep_hi = k0 + 2 * w + 1 < left ? 0xFFFF0000u : 0u;
+              v[w] &= keep_lo | keep_hi;
+            }
+          }
+          af[i] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, tr_frag(bs, BN * 2, wn * C::WTN + j * 32, ks));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < nk) {
+        wait_vmcnt_lds<0>();
+        bare_barrier();
+      }
+    }
+    (void)OPS;
+    lds_barrier();  // every wave is done with the ring before the epilogue stages through it
+    TileCoord tc;
+    tc.e = e;
+    tc.mi = 0;
+    tc.row0 = (int64_t)e * g.P + m0;
+    tc.rows_valid = (int)(g.P - m0 < BM ? g.P - m0 : BM);
+    tc.n0 = n0;
+    epilogue<C>(acc, smem, ge, tc);
+  }
+}
+
 template <class C, typename Kern>
 hipError_t launch_kernel(Kern kern, bool* attr_done, const GemmArgs& g, hipStream_t stream) {
   const int dev = current_device();
@@ -752,7 +935,42 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
   return launch_kernel<RegsTile<GATED>>(grouped_gemm_regs_kernel<RegsTile<GATED>, B_NMAJOR>, done, g, stream);
 }
 
+using WgradTile = Tile<256, 256, 2, 4, 2, false>;
+
 }  // namespace
+
+hipError_t launch_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, bool w_out_in,
+                                int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
+                                hipStream_t stream) {
+  // dX_e = dY_e W_e^T: A = dy [cap, d_out] (K = d_out), N = d_in, out dx [cap, d_in]
+  if (!w_out_in) {
+    // w [E, d_in, d_out]: row n of the operand is W_e row n, K-contiguous
+    const GemmArgs g{dy, d_out, nullptr, 1, 0, w, d_in * d_out, d_out, 0, d_in, d_out, offsets, E, cap_rows, dx, d_in};
+    return launch_grouped<false, false>(g, stream);
+  }
+  // w [E, d_out, d_in]: K rows of N-contiguous columns, as the down projection's weights
+  const GemmArgs g{dy, d_out, nullptr, 1, 0, w, d_in * d_out, d_in, 0, d_in, d_out, offsets, E, cap_rows, dx, d_in};
+  return launch_grouped<false, true>(g, stream);
+}
+
+hipError_t launch_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, bool w_out_in,
+                                int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
+                                hipStream_t stream) {
+  // [E, d_in, d_out] = X^T dY per expert, or its transpose [E, d_out, d_in] = dY^T X
+  const WgradArgs g = !w_out_in ? WgradArgs{x, d_in, dy, d_out, d_in, d_out, offsets, E, cap_rows, dw}
+                                : WgradArgs{dy, d_out, x, d_in, d_out, d_in, offsets, E, cap_rows, dw};
+  static bool done[64] = {};
+  const int dev = current_device();
+  if (dev >= 0 && dev < 64 && !done[dev]) {
+    hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_wgrad_kernel<WgradTile>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, WgradTile::LDS_BYTES);
+    if (st != hipSuccess) return st;
+    done[dev] = true;
+  }
+  hipLaunchKernelGGL(grouped_wgrad_kernel<WgradTile>, dim3(device_cu_count(dev)), dim3(WgradTile::THREADS),
+                     WgradTile::LDS_BYTES, stream, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
                                  int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,

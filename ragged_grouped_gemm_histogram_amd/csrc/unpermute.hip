@@ -4,7 +4,9 @@
 // write the same element. Each thread owns 8 consecutive columns of one token
 // and accumulates sum_j w[t,j] * y_perm[inv[t,j]] in fp32 registers, j
 // ascending, skipping slots whose inverse-map entry is outside [0, T*k); the
-// k gathered rows are never materialised.
+// k gathered rows are never materialised. With no weights (a null pointer)
+// the same kernel is the backward of the forward's row gather: a token's
+// gradient is the plain sum of its kept slots' rows.
 
 #include "common.h"
 
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const uint16_t* __r
       for (int j = 0; j < k; ++j) {
         const int64_t p = inv[t * k + j];
         if (p < 0 || p >= S) continue;
-        const float wt = w[t * k + j];
+        const float wt = w != nullptr ? w[t * k + j] : 1.0f;
         const u32x4 v = *reinterpret_cast<const u32x4*>(y_perm + p * d + ch * 8);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -53,7 +55,63 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const uint16_t* __r
   }
 }
 
+// Backward of the weighted scatter-back, one wave per token: for every kept
+// slot j, dy_perm[inv[t,j]] = bf16(w[t,j] * dy[t]) (each sorted row has one
+// owner slot, so rows are written once and without atomics) and the routing
+// weight gradient dw[t,j] = sum_c dy[t,c] * y_perm[inv[t,j],c], an fp32 dot
+// product reduced across the wave; dropped slots get dw = 0.
+__global__ __launch_bounds__(kThreads) void unpermute_backward_kernel(
+    const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y_perm, const int32_t* __restrict__ inv,
+    const float* __restrict__ w, int64_t T, int k, int64_t d, uint16_t* __restrict__ dy_perm, float* __restrict__ dw) {
+  constexpr int kWaves = kThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t S = T * k;
+  const int64_t cpr = d / 8;
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  for (int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); t < T; t += nwaves) {
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = inv[t * k + j];
+      if (p < 0 || p >= S) {
+        if (lane == 0) dw[t * k + j] = 0.f;
+        continue;
+      }
+      const float wt = w[t * k + j];
+      float dot = 0.f;
+      for (int64_t ch = lane; ch < cpr; ch += 64) {
+        const u32x4 g = *reinterpret_cast<const u32x4*>(dy + t * d + ch * 8);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(y_perm + p * d + ch * 8);
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float g0 = bf16_bits_to_f32(g[q] & 0xFFFFu), g1 = bf16_bits_to_f32(g[q] >> 16);
+          dot = fmaf(g0, bf16_bits_to_f32(v[q] & 0xFFFFu), dot);
+          dot = fmaf(g1, bf16_bits_to_f32(v[q] >> 16), dot);
+          o[q] = pack_bf16x2(wt * g0, wt * g1);
+        }
+        *reinterpret_cast<u32x4*>(dy_perm + p * d + ch * 8) = o;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+      if (lane == 0) dw[t * k + j] = dot;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_unpermute_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* inv, const float* w,
+                                     int64_t T, int32_t k, int64_t d, uint16_t* dy_perm, float* dw,
+                                     hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int dev = current_device();
+  constexpr int kWaves = kThreads / 64;
+  int64_t blocks = (T + kWaves - 1) / kWaves;
+  const int64_t cap = (int64_t)device_cu_count(dev) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(unpermute_backward_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, dy, y_perm, inv, w,
+                     T, k, d, dy_perm, dw);
+  return hipGetLastError();
+}
 
 hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* inv, const float* w, int64_t T, int32_t k,
                             int64_t d, uint16_t* y, hipStream_t stream) {

@@ -133,3 +133,66 @@ def test_binding_rejects_bad_tensors():
     x = torch.zeros((4, 8), dtype=torch.float32)
     with pytest.raises((TypeError, ValueError)):
         moe.moe_permute(x, torch.zeros((4, 2), dtype=torch.int32), 4)
+
+
+def dgrad(lib, dy=FAKE, offs=FAKE, w=FAKE, layout=0, cap=16, d_in=16, d_out=24, E=2, dx=FAKE):
+    return lib.moe_grouped_dgrad(dy, offs, w, layout, cap, d_in, d_out, E, dx, None)
+
+
+def wgrad(lib, x=FAKE, dy=FAKE, offs=FAKE, layout=0, cap=16, d_in=16, d_out=24, E=2, dw=FAKE):
+    return lib.moe_grouped_wgrad(x, dy, offs, layout, cap, d_in, d_out, E, dw, None)
+
+
+@pytest.mark.parametrize("fn", [dgrad, wgrad])
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=2), SHAPE), (dict(layout=-1), SHAPE), (dict(cap=-1), SHAPE), (dict(d_in=12), SHAPE),
+    (dict(d_out=0), SHAPE), (dict(E=0), SHAPE), (dict(E=1025), SHAPE),
+    (dict(offs=None), NULLP), (dict(dy=None), NULLP), (dict(offs=FAKE + 2), ALIGN), (dict(dy=FAKE + 8), ALIGN),
+])
+def test_backward_gemm_validation(lib, fn, kw, status):
+    assert fn(lib, **kw) == status
+
+
+def test_backward_gemm_operand_checks(lib):
+    assert dgrad(lib, w=None) == NULLP and dgrad(lib, dx=None) == NULLP and dgrad(lib, w=FAKE + 4) == ALIGN
+    assert wgrad(lib, x=None) == NULLP and wgrad(lib, dw=None) == NULLP and wgrad(lib, x=FAKE + 2) == ALIGN
+    # an empty capacity needs no row buffers (Wgrad still writes E * d_in * d_out zeros)
+    assert dgrad(lib, dy=None, dx=None, cap=0) in (OK, DEV)
+    assert wgrad(lib, x=None, dy=None, cap=0) in (OK, DEV)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(d=6), SHAPE),
+    (dict(g=None), NULLP), (dict(inv=None), NULLP), (dict(dx=None), NULLP),
+    (dict(g=FAKE + 2), ALIGN), (dict(dx=FAKE + 8), ALIGN), (dict(inv=FAKE + 2), ALIGN),
+])
+def test_permute_backward_validation(lib, kw, status):
+    a = dict(g=FAKE, inv=FAKE, T=4, k=2, d=8, dx=FAKE)
+    a.update(kw)
+    assert lib.moe_permute_backward(a["g"], a["inv"], a["T"], a["k"], a["d"], a["dx"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(d=4), SHAPE),
+    (dict(dy=None), NULLP), (dict(yp=None), NULLP), (dict(inv=None), NULLP), (dict(w=None), NULLP),
+    (dict(dyp=None), NULLP), (dict(dw=None), NULLP),
+    (dict(dy=FAKE + 8), ALIGN), (dict(yp=FAKE + 2), ALIGN), (dict(dyp=FAKE + 4), ALIGN), (dict(dw=FAKE + 2), ALIGN),
+])
+def test_unpermute_backward_validation(lib, kw, status):
+    a = dict(dy=FAKE, yp=FAKE, inv=FAKE, w=FAKE, T=4, k=2, d=8, dyp=FAKE, dw=FAKE)
+    a.update(kw)
+    assert lib.moe_unpermute_backward(a["dy"], a["yp"], a["inv"], a["w"], a["T"], a["k"], a["d"], a["dyp"], a["dw"],
+                                      None) == status
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour on a host without a GPU")
+def test_backward_device_check_without_gpu(lib):
+    assert dgrad(lib) == DEV and wgrad(lib) == DEV
+    assert lib.moe_permute_backward(FAKE, FAKE, 4, 2, 8, FAKE, None) == DEV
+    assert lib.moe_unpermute_backward(FAKE, FAKE, FAKE, FAKE, 4, 2, 8, FAKE, FAKE, None) == DEV
+
+
+def test_binding_backward_rejects_bad_layout():
+    w = torch.zeros((2, 16, 24), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_grouped_dgrad(torch.zeros((4, 24), dtype=torch.bfloat16), torch.zeros(3, dtype=torch.int32), w, "io")
