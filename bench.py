@@ -102,8 +102,9 @@ def main(argv=None):
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--sweep", choices=SWEEPS,
-                    help="instead of the step, run one single-projection sweep and print its own JSON line: "
-                         "histogram (Fig 40), capacity (Fig 38) or decomposition (Fig 39)")
+                    help="instead of the step, run one sweep and print its own JSON line: histogram (Fig 40), "
+                         "capacity (Fig 38) or decomposition (Fig 39) of one grouped projection, or the step's "
+                         "backward kernels (Eq 15)")
     ap.add_argument("--sweep-samples", type=int, default=20, help="timed samples per sweep point")
     ap.add_argument("--sweep-warmup", type=int, default=10, help="warm-up samples per sweep point")
     args = ap.parse_args(argv)
@@ -542,7 +543,72 @@ def sweep_decomposition(torch, moe, dev, warmup, samples):
             "gate_overruns": timer.gate_overruns, "points": points}
 
 
-SWEEPS = {"histogram": sweep_histogram, "capacity": sweep_capacity, "decomposition": sweep_decomposition}
+def sweep_backward(torch, moe, dev, warmup, samples):
+    """The expert step's backward kernels on the zipf64 workload (OLMo report Sec 9.5, Eq 15): the
+    unpermute backward, Dgrad and Wgrad of the down projection ([E, h, d]) and of the gate/up
+    projection ([E, 2h, d]), and the permute backward, each timed on its own (queued samples,
+    HIP events). Useful FLOPs of the four GEMMs: 2*M*d_in*d_out each, 12*M*d*h together. The SwiGLU
+    backward between the two projections is not part of this library."""
+    import numpy as np
+
+    from workloads import make_workload
+
+    wl = make_workload("zipf64")
+    T, k, E, d, h = wl.T, wl.k, wl.E, wl.d, wl.h
+    S = T * k
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w_ug, w_down = bf(wl.x), bf(wl.w_ug), bf(wl.w_down)
+    ids = torch.from_numpy(wl.expert_ids).to(dev)
+    rw = torch.from_numpy(wl.routing_w).to(dev)
+    y, p, h_buf, y_perm = moe.moe_expert_forward(x, ids, rw, w_ug, w_down, fused_gather=False)
+    M = int(p.offsets[-1].item())
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    dy = torch.randn((T, d), generator=g, device=dev).to(torch.bfloat16)
+    d_u = torch.randn((S, 2 * h), generator=g, device=dev).to(torch.bfloat16)  # stands in for the SwiGLU backward
+    dy_perm = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+    d_rw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dh = torch.empty((S, h), dtype=torch.bfloat16, device=dev)
+    dxp = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    dwd = torch.empty_like(w_down)
+    dwu = torch.empty_like(w_ug)
+    timer = QueuedTimer(torch)
+    stages = [
+        ("unpermute_backward", lambda: moe.moe_unpermute_backward(dy, y_perm, p.inv_map, rw, dy_perm=dy_perm,
+                                                                  d_routing_w=d_rw), None,
+         2 * T * d + 4 * M * d + 16 * S),
+        ("dgrad_down", lambda: moe.moe_grouped_dgrad(dy_perm, p.offsets, w_down, "in_out", dx=dh), 2 * M * h * d, None),
+        ("wgrad_down", lambda: moe.moe_grouped_wgrad(h_buf, dy_perm, p.offsets, "in_out", dw=dwd), 2 * M * h * d, None),
+        ("dgrad_gate_up", lambda: moe.moe_grouped_dgrad(d_u, p.offsets, w_ug, "out_in", dx=dxp), 4 * M * h * d, None),
+        ("wgrad_gate_up", lambda: moe.moe_grouped_wgrad(p.x_perm, d_u, p.offsets, "out_in", dw=dwu), 4 * M * h * d,
+         None),
+        ("permute_backward", lambda: moe.moe_permute_backward(dxp, p.inv_map, dx=dx), None, 2 * M * d + 2 * T * d + 4 * S),
+    ]
+    res, gemm_ms, gemm_flops = {}, 0.0, 0
+    for name, fn, flops, nbytes in stages:
+        r = timer(fn, warmup, samples)
+        entry = {"ms": r["mean_ms"], "median_ms": r["median_ms"]}
+        if flops:
+            entry["TFLOP/s"] = flops / r["mean_ms"] / 1e9
+            gemm_ms += r["mean_ms"]
+            gemm_flops += flops
+        else:
+            entry["GB/s"] = nbytes / r["mean_ms"] / 1e6
+        res[name] = entry
+        _progress(f"backward: {name} {r['mean_ms']:.4f} ms")
+    return {"metric": "useful TFLOP/s of the expert step's four backward GEMMs (12*M*d*h)", "sweep": "backward",
+            "value": gemm_flops / gemm_ms / 1e9, "unit": "TFLOP/s", "data": "synthetic", "dtype": "bf16",
+            "config": {"workload": "zipf64 backward", "T": T, "k": k, "E": E, "d": d, "h": h, "M": M,
+                       "warmup": warmup, "samples": samples},
+            "gemm_ms": gemm_ms, "stages": res, "gate_overruns": timer.gate_overruns}
+
+
+SWEEPS = {"histogram": sweep_histogram, "capacity": sweep_capacity, "decomposition": sweep_decomposition,
+          "backward": sweep_backward}
 
 
 if __name__ == "__main__":
