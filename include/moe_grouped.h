@@ -60,7 +60,7 @@ typedef enum moe_status {
                                      T*k >= 2^31, or cap_rows < 0                               */
   MOE_ERR_MISALIGNED = 3,         /* a bf16 tensor not 16-byte aligned, or an int32/float
                                      tensor not 4-byte aligned                                  */
-  MOE_ERR_WORKSPACE = 4,          /* workspace_bytes < moe_permute_workspace_bytes(T, k, E)     */
+  MOE_ERR_WORKSPACE = 4,          /* workspace_bytes below the call's *_workspace_bytes()       */
   MOE_ERR_UNSUPPORTED_DEVICE = 5, /* the current HIP device is not gfx950, or no device         */
   MOE_ERR_LAUNCH = 6              /* a HIP error was reported while launching                    */
 } moe_status;
@@ -202,20 +202,30 @@ moe_status moe_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const u
                              int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
                              hipStream_t stream);
 
+/* Bytes of device workspace moe_grouped_wgrad needs (fp32 partial gradients
+ * of experts whose rows are split; 0 when cap_rows <= 4096). Host arithmetic
+ * only; 0 for invalid shapes. */
+size_t moe_grouped_wgrad_workspace_bytes(int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E);
+
 /* Wgrad: dW_e = bf16(x[rows_e]^T * dy[rows_e]), written [E, d_in, d_out]
  * (MOE_W_IN_OUT) or transposed [E, d_out, d_in] (MOE_W_OUT_IN), so the
  * gradient has the layout of the weight it belongs to.
  *
- *   x        bf16  [cap_rows, d_in]    the projection's input rows
- *   dy       bf16  [cap_rows, d_out]   the gradient of its output rows
- *   offsets  int32 [E+1]
- *   dw       bf16  [E * d_in * d_out]  out, every element written; an expert
- *                                     with no rows gets zeros
+ *   x          bf16  [cap_rows, d_in]    the projection's input rows
+ *   dy         bf16  [cap_rows, d_out]   the gradient of its output rows
+ *   offsets    int32 [E+1]
+ *   dw         bf16  [E * d_in * d_out]  out, every element written; an
+ *                                       expert with no rows gets zeros
+ *   workspace  at least moe_grouped_wgrad_workspace_bytes(...) bytes,
+ *              16-byte aligned (may be NULL when that is 0)
  *
- * One persistent launch over 256 x 256 output tiles, largest experts first. */
+ * One persistent launch over 256 x 256 output tiles, largest experts first;
+ * an expert with more than 4096 rows is split into row chunks whose fp32
+ * partials a second launch sums in chunk order before the one rounding to
+ * bf16, so the result is deterministic. */
 moe_status moe_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, int32_t w_layout,
                              int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
-                             hipStream_t stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward of moe_permute's row gather (x_perm[p] = x[perm[p] / k]):
  * dx[t] = bf16(sum over kept j, ascending, of dx_perm[inv_map[t, j]]), fp32

@@ -37,7 +37,8 @@ _SIGNATURES = {
                                      [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_unpermute": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
     "moe_grouped_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]),
-    "moe_grouped_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_grouped_wgrad_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "moe_grouped_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _sz, _vp]),
     "moe_permute_backward": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _vp, _vp]),
     "moe_unpermute_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -290,8 +291,12 @@ def moe_grouped_dgrad(dy: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor, 
     return dx
 
 
+def wgrad_workspace_bytes(cap_rows: int, d_in: int, d_out: int, E: int) -> int:
+    return int(load_library().moe_grouped_wgrad_workspace_bytes(cap_rows, d_in, d_out, E))
+
+
 def moe_grouped_wgrad(x: torch.Tensor, dy: torch.Tensor, offsets: torch.Tensor, layout: str = "in_out", *,
-                      dw=None) -> torch.Tensor:
+                      dw=None, workspace=None) -> torch.Tensor:
     """dW_e = bf16(X[rows_e]^T @ dY[rows_e]) in the weight's layout; zeros for experts with no rows (one launch)."""
     if x.dim() != 2 or dy.dim() != 2 or offsets.dim() != 1:
         raise ValueError("expected x [cap, d_in], dy [cap, d_out] and offsets [E+1]")
@@ -306,8 +311,14 @@ def moe_grouped_wgrad(x: torch.Tensor, dy: torch.Tensor, offsets: torch.Tensor, 
     if layout not in W_LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(W_LAYOUTS)}, got {layout!r}")
     dw = _out(dw, "dw", torch.bfloat16, shape, dev)
+    need = wgrad_workspace_bytes(cap, d_in, d_out, E)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes on {dev}")
     _check(load_library().moe_grouped_wgrad(_ptr(x), _ptr(dy), _ptr(offsets), W_LAYOUTS[layout], cap, d_in, d_out, E,
-                                            _ptr(dw), _stream(x)), "moe_grouped_wgrad")
+                                            _ptr(dw), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(x)), "moe_grouped_wgrad")
     return dw
 
 
@@ -364,6 +375,6 @@ __all__ = [
     "LIB_PATH", "MAX_EXPERTS", "MoeError", "Permuted", "grouped_swiglu_expert", "header_functions", "load_library",
     "grouped_swiglu_expert_gather", "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu",
     "moe_gemm_up_swiglu_gather", "moe_permute", "moe_unpermute",
-    "permute_workspace_bytes", "W_LAYOUTS", "moe_grouped_dgrad", "moe_grouped_wgrad", "moe_permute_backward",
+    "permute_workspace_bytes", "W_LAYOUTS", "moe_grouped_dgrad", "moe_grouped_wgrad", "moe_permute_backward", "wgrad_workspace_bytes",
     "moe_unpermute_backward",
 ]

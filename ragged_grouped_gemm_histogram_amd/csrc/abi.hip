@@ -190,19 +190,29 @@ moe_status moe_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const u
   return launched(launch_grouped_dgrad(dy, offsets, w, w_layout == MOE_W_OUT_IN, cap_rows, d_in, d_out, E, dx, stream));
 }
 
+size_t moe_grouped_wgrad_workspace_bytes(int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E) {
+  if (check_gemm_shape(cap_rows, d_in, d_out, E) != MOE_OK) return 0;
+  return (size_t)wgrad_partial_slots(cap_rows) * (size_t)d_in * (size_t)d_out * sizeof(float);
+}
+
 moe_status moe_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, int32_t w_layout,
                              int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
-                             hipStream_t stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (w_layout != MOE_W_IN_OUT && w_layout != MOE_W_OUT_IN) return MOE_ERR_BAD_SHAPE;
   moe_status st = check_gemm_shape(cap_rows, d_in, d_out, E);
   if (st != MOE_OK) return st;
+  const size_t need = moe_grouped_wgrad_workspace_bytes(cap_rows, d_in, d_out, E);
   if (missing(x, cap_rows * d_in) || missing(dy, cap_rows * d_out) || missing(offsets, E + 1) ||
-      missing(dw, (int64_t)E * d_in * d_out))
+      missing(dw, (int64_t)E * d_in * d_out) || missing(workspace, (int64_t)need))
     return MOE_ERR_NULL_POINTER;
-  if (misaligned(x, 16) || misaligned(dy, 16) || misaligned(dw, 16) || misaligned(offsets, 4)) return MOE_ERR_MISALIGNED;
+  if (misaligned(x, 16) || misaligned(dy, 16) || misaligned(dw, 16) || misaligned(offsets, 4) ||
+      misaligned(workspace, 16))
+    return MOE_ERR_MISALIGNED;
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if ((st = check_device()) != MOE_OK) return st;
   (void)hipGetLastError();
-  return launched(launch_grouped_wgrad(x, dy, offsets, w_layout == MOE_W_OUT_IN, cap_rows, d_in, d_out, E, dw, stream));
+  return launched(launch_grouped_wgrad(x, dy, offsets, w_layout == MOE_W_OUT_IN, cap_rows, d_in, d_out, E, dw,
+                                       static_cast<float*>(workspace), stream));
 }
 
 moe_status moe_permute_backward(const uint16_t* dx_perm, const int32_t* inv_map, int64_t T, int32_t k, int64_t d,
@@ -242,7 +252,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_NULL_POINTER: return "MOE_ERR_NULL_POINTER: a pointer is NULL while its tensor is non-empty";
     case MOE_ERR_BAD_SHAPE: return "MOE_ERR_BAD_SHAPE: a size is out of range (T, k, E, d, h or T*k)";
     case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: a bf16 tensor is not 16-byte aligned or an int32/fp32 tensor not 4-byte aligned";
-    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_permute_workspace_bytes()";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than the call's *_workspace_bytes()";
     case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE: the current HIP device is not gfx950";
     case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: a kernel launch reported a HIP error";
   }

@@ -60,9 +60,13 @@ hipError_t launch_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, 
 hipError_t launch_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, bool w_out_in,
                                 int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
                                 hipStream_t stream);
+// Wgrad splits experts with more than kWgradChunk rows; their fp32 partials need
+// wgrad_partial_slots(cap_rows) slots of d_in * d_out floats.
+constexpr int kWgradChunk = 4096;
+int64_t wgrad_partial_slots(int64_t cap_rows);
 hipError_t launch_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, bool w_out_in,
                                 int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
-                                hipStream_t stream);
+                                float* partial, hipStream_t stream);
 hipError_t launch_gemm_down(const uint16_t* h_buf, const int32_t* offsets, const uint16_t* w_down,
                             int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* y_perm,
                             hipStream_t stream);

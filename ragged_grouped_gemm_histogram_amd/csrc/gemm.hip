@@ -706,6 +706,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs 
 // forward do. The ragged contraction length is handled by clamping the rows a
 // tail stage loads to the expert's last row and zeroing A's fragment entries
 // past the block, so every product with a padded row is an exact zero.
+//
+// An expert with more than kWgradChunk rows is split along its rows into
+// chunks of at most kWgradChunk: every chunk writes an fp32 partial gradient
+// into the workspace and a second kernel sums an expert's partials in chunk
+// order and rounds once to bf16 (deterministic, no atomics). Without the
+// split the largest expert's tiles would each contract over all its rows and
+// finish long after the rest of the grid.
 // ============================================================================
 struct WgradArgs {
   const uint16_t* A;  // [cap_rows, P]
@@ -717,7 +724,42 @@ struct WgradArgs {
   int32_t E;
   int64_t cap_rows;
   uint16_t* out;      // [E, P, Q]
+  float* partial;     // [slots, P, Q] fp32 partial gradients of split experts
+  int64_t slots;
 };
+
+// Per-expert row blocks, chunk counts and partial-slot bases from the device
+// offsets (clamped as in the forward), in LDS. Experts are split in index
+// order: slot_base[e] is the first partial slot of a split expert (-1 if the
+// expert is not split). Identical in both Wgrad kernels.
+struct WgradPlan {
+  int lo[MOE_MAX_EXPERTS];
+  int rows[MOE_MAX_EXPERTS];
+  int chunks[MOE_MAX_EXPERTS];
+  int slot_base[MOE_MAX_EXPERTS];
+};
+
+template <int THREADS>
+__device__ void build_wgrad_plan(const WgradArgs& g, WgradPlan& pl) {
+  for (int e = threadIdx.x; e < g.E; e += THREADS) {
+    int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
+    lo = lo < 0 ? 0 : (lo > g.cap_rows ? g.cap_rows : lo);
+    hi = hi < lo ? lo : (hi > g.cap_rows ? g.cap_rows : hi);
+    const int rows = (int)(hi - lo);
+    pl.lo[e] = (int)lo;
+    pl.rows[e] = rows;
+    pl.chunks[e] = rows > kWgradChunk ? (rows + kWgradChunk - 1) / kWgradChunk : 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int next = 0;
+    for (int e = 0; e < g.E; ++e) {
+      pl.slot_base[e] = pl.chunks[e] > 1 ? next : -1;
+      if (pl.chunks[e] > 1) next += pl.chunks[e];
+    }
+  }
+  __syncthreads();
+}
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_wgrad_kernel(WgradArgs g) {
@@ -726,47 +768,57 @@ __global__ __launch_bounds__(C::THREADS) void grouped_wgrad_kernel(WgradArgs g) 
   static_assert(BM * 2 <= 1024 && BN * 2 <= 1024, "a stage row must fit one wave load");
   constexpr int OPS = C::A_OPS + C::B_OPS;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  __shared__ int s_lo[MOE_MAX_EXPERTS], s_rows[MOE_MAX_EXPERTS], s_order[MOE_MAX_EXPERTS];
+  __shared__ WgradPlan pl;
+  __shared__ int s_order[MOE_MAX_EXPERTS];
+  __shared__ int s_item_end[MOE_MAX_EXPERTS];  // inclusive prefix of work items over s_order
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-  // Clamped row block of every expert, then the experts in descending row
-  // count (ties by index): dealing the largest contractions first keeps the
-  // static round-robin schedule balanced.
+  build_wgrad_plan<C::THREADS>(g, pl);
+  // Experts in descending row count (ties by index): dealing the largest
+  // contractions first keeps the static round-robin schedule balanced.
   for (int e = tid; e < g.E; e += C::THREADS) {
-    int64_t lo = g.offsets[e], hi = g.offsets[e + 1];
-    lo = lo < 0 ? 0 : (lo > g.cap_rows ? g.cap_rows : lo);
-    hi = hi < lo ? lo : (hi > g.cap_rows ? g.cap_rows : hi);
-    s_lo[e] = (int)lo;
-    s_rows[e] = (int)(hi - lo);
-  }
-  __syncthreads();
-  for (int e = tid; e < g.E; e += C::THREADS) {
-    const int re = s_rows[e];
+    const int re = pl.rows[e];
     int rank = 0;
     for (int f = 0; f < g.E; ++f) {
-      const int rf = s_rows[f];
+      const int rf = pl.rows[f];
       rank += (rf > re || (rf == re && f < e)) ? 1 : 0;
     }
     s_order[rank] = e;
   }
   __syncthreads();
-
   const int64_t m_tiles = (g.P + BM - 1) / BM, n_tiles = (g.Q + BN - 1) / BN;
-  const int64_t per_expert = m_tiles * n_tiles;
-  const int64_t total_tiles = per_expert * g.E;
+  const int per_chunk = (int)(m_tiles * n_tiles);  // output tiles of one expert (or one chunk of it)
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < g.E; ++i) {
+      run += pl.chunks[s_order[i]] * per_chunk;
+      s_item_end[i] = run;
+    }
+  }
+  __syncthreads();
+  const int total_items = __builtin_amdgcn_readfirstlane(s_item_end[g.E - 1]);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const GemmArgs ge{nullptr, 0, nullptr, 1, 0, nullptr, 0, 0, 0, g.Q, 0, nullptr, g.E, 0, g.out, g.Q};
 
-  for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
-    const int pos = (int)(t / per_expert);
-    const int64_t rem = t - (int64_t)pos * per_expert;
+  for (int64_t t = logical_worker(); t < total_items; t += gridDim.x) {
+    int lo_i = 0, hi_i = g.E - 1;  // first position whose item range ends after t
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if (s_item_end[mid] > t) hi_i = mid; else lo_i = mid + 1;
+    }
+    const int pos = lo_i;
+    const int64_t rem0 = t - (pos > 0 ? s_item_end[pos - 1] : 0);
     const int e = __builtin_amdgcn_readfirstlane(s_order[pos]);
-    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e]);
-    const int rows = __builtin_amdgcn_readfirstlane(s_rows[e]);
+    const int chunk = __builtin_amdgcn_readfirstlane((int)(rem0 / per_chunk));
+    const int64_t rem = rem0 - (int64_t)chunk * per_chunk;
+    const int lo = __builtin_amdgcn_readfirstlane(pl.lo[e] + chunk * kWgradChunk);
+    const int all_rows = pl.rows[e] - chunk * kWgradChunk;
+    const int rows = __builtin_amdgcn_readfirstlane(all_rows < kWgradChunk ? all_rows : kWgradChunk);
+    const int slot_base = __builtin_amdgcn_readfirstlane(pl.slot_base[e]);
     const int64_t m0 = (rem / n_tiles) * BM, n0 = (rem % n_tiles) * BN;
     const int nk = (rows + BK - 1) / BK;
 
@@ -875,13 +927,73 @@ __global__ __launch_bounds__(C::THREADS) void grouped_wgrad_kernel(WgradArgs g) 
     }
     (void)OPS;
     lds_barrier();  // every wave is done with the ring before the epilogue stages through it
-    TileCoord tc;
-    tc.e = e;
-    tc.mi = 0;
-    tc.row0 = (int64_t)e * g.P + m0;
-    tc.rows_valid = (int)(g.P - m0 < BM ? g.P - m0 : BM);
-    tc.n0 = n0;
-    epilogue<C>(acc, smem, ge, tc);
+    if (slot_base >= 0) {
+      // A chunk of a split expert: fp32 partial straight from the accumulators. Lane l holds
+      // row m0 + wm*WTM + 32i + l%32, columns n0 + wn*WTN + 32j + 8q + 4(l/32) + 0..3.
+      const int64_t slot = slot_base + chunk;
+      if (slot < g.slots) {
+        float* dst = g.partial + slot * g.P * g.Q;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          const int64_t row = m0 + wm * C::WTM + i * 32 + (lane & 31);
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t col = n0 + wn * C::WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+              if (row < g.P && col < g.Q) {
+                const float4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                *reinterpret_cast<float4*>(dst + row * g.Q + col) = v;
+              }
+            }
+        }
+      }
+    } else {
+      TileCoord tc;
+      tc.e = e;
+      tc.mi = 0;
+      tc.row0 = (int64_t)e * g.P + m0;
+      tc.rows_valid = (int)(g.P - m0 < BM ? g.P - m0 : BM);
+      tc.n0 = n0;
+      epilogue<C>(acc, smem, ge, tc);
+    }
+  }
+}
+
+// Second Wgrad pass: each split expert's gradient is the sum of its chunk
+// partials, taken in chunk order in fp32 and rounded once to bf16.
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradArgs g) {
+  __shared__ WgradPlan pl;
+  __shared__ int s_split[MOE_MAX_EXPERTS];
+  __shared__ int s_nsplit;
+  build_wgrad_plan<256>(g, pl);
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int e = 0; e < g.E; ++e)
+      if (pl.slot_base[e] >= 0) s_split[n++] = e;
+    s_nsplit = n;
+  }
+  __syncthreads();
+  const int64_t groups = g.P * g.Q / 8;  // 8 consecutive elements per thread step (Q % 8 == 0)
+  const int64_t total = (int64_t)s_nsplit * groups;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int se = (int)(i / groups);
+    const int64_t el = (i - (int64_t)se * groups) * 8;
+    const int e = s_split[se];
+    const int base = pl.slot_base[e];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < pl.chunks[e]; ++c) {
+      if (base + c >= g.slots) break;
+      const float* src = g.partial + (int64_t)(base + c) * g.P * g.Q + el;
+      const float4 a = *reinterpret_cast<const float4*>(src);
+      const float4 b = *reinterpret_cast<const float4*>(src + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *reinterpret_cast<u32x4*>(g.out + (int64_t)e * g.P * g.Q + el) = o;
   }
 }
 
@@ -953,12 +1065,19 @@ hipError_t launch_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, cons
   return launch_grouped<false, true>(g, stream);
 }
 
+int64_t wgrad_partial_slots(int64_t cap_rows) {
+  // A split expert has more than kWgradChunk rows and at most rows / kWgradChunk + 1 < 2 rows / kWgradChunk
+  // chunks, so all split experts together hold fewer than 2 * cap_rows / kWgradChunk chunks.
+  return cap_rows > kWgradChunk ? (2 * cap_rows + kWgradChunk - 1) / kWgradChunk : 0;
+}
+
 hipError_t launch_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int32_t* offsets, bool w_out_in,
                                 int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dw,
-                                hipStream_t stream) {
+                                float* partial, hipStream_t stream) {
   // [E, d_in, d_out] = X^T dY per expert, or its transpose [E, d_out, d_in] = dY^T X
-  const WgradArgs g = !w_out_in ? WgradArgs{x, d_in, dy, d_out, d_in, d_out, offsets, E, cap_rows, dw}
-                                : WgradArgs{dy, d_out, x, d_in, d_out, d_in, offsets, E, cap_rows, dw};
+  const int64_t slots = wgrad_partial_slots(cap_rows);
+  const WgradArgs g = !w_out_in ? WgradArgs{x, d_in, dy, d_out, d_in, d_out, offsets, E, cap_rows, dw, partial, slots}
+                                : WgradArgs{dy, d_out, x, d_in, d_out, d_in, offsets, E, cap_rows, dw, partial, slots};
   static bool done[64] = {};
   const int dev = current_device();
   if (dev >= 0 && dev < 64 && !done[dev]) {
@@ -969,6 +1088,11 @@ hipError_t launch_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int
   }
   hipLaunchKernelGGL(grouped_wgrad_kernel<WgradTile>, dim3(device_cu_count(dev)), dim3(WgradTile::THREADS),
                      WgradTile::LDS_BYTES, stream, g);
+  if (slots > 0) {
+    hipError_t st = hipGetLastError();
+    if (st != hipSuccess) return st;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(device_cu_count(dev) * 4), dim3(256), 0, stream, g);
+  }
   return hipGetLastError();
 }
 

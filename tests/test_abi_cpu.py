@@ -139,8 +139,24 @@ def dgrad(lib, dy=FAKE, offs=FAKE, w=FAKE, layout=0, cap=16, d_in=16, d_out=24, 
     return lib.moe_grouped_dgrad(dy, offs, w, layout, cap, d_in, d_out, E, dx, None)
 
 
-def wgrad(lib, x=FAKE, dy=FAKE, offs=FAKE, layout=0, cap=16, d_in=16, d_out=24, E=2, dw=FAKE):
-    return lib.moe_grouped_wgrad(x, dy, offs, layout, cap, d_in, d_out, E, dw, None)
+def wgrad(lib, x=FAKE, dy=FAKE, offs=FAKE, layout=0, cap=16, d_in=16, d_out=24, E=2, dw=FAKE, ws=FAKE,
+          wsb=1 << 30):
+    return lib.moe_grouped_wgrad(x, dy, offs, layout, cap, d_in, d_out, E, dw, ws, wsb, None)
+
+
+def test_wgrad_workspace_bytes(lib):
+    f = moe.wgrad_workspace_bytes
+    assert f(4096, 64, 64, 4) == 0  # no expert can exceed 4096 rows
+    assert f(4097, 64, 64, 4) == 3 * 64 * 64 * 4  # ceil(2 * 4097 / 4096) slots
+    assert f(65536, 2048, 1536, 64) == 32 * 2048 * 1536 * 4
+    assert f(-1, 64, 64, 4) == 0 and f(100, 12, 64, 4) == 0 and f(100, 64, 64, 0) == 0
+
+
+def test_wgrad_workspace_validation(lib):
+    assert wgrad(lib, cap=65536, ws=None) == NULLP
+    assert wgrad(lib, cap=65536, wsb=100) == WS
+    assert wgrad(lib, cap=65536, ws=FAKE + 8) == ALIGN
+    assert wgrad(lib, cap=100, ws=None, wsb=0) in (OK, DEV)  # nothing to split: no workspace needed
 
 
 @pytest.mark.parametrize("fn", [dgrad, wgrad])

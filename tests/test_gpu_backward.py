@@ -41,8 +41,9 @@ CASES = [
     ([1], 64, 64),                                  # one row
     ([64, 128, 65, 63], 264, 136),                  # contraction lengths at and around one stage
     ([3000] * 3 + [0] * 2 + [17], 512, 768),        # many stages per expert, several output tiles
+    ([9000, 0, 4097, 4096, 8192, 3], 256, 264),     # Wgrad splits experts above 4096 rows into chunks
 ]
-IDS = ["ragged", "big", "k-tail", "one-row", "stage-edges", "deep"]
+IDS = ["ragged", "big", "k-tail", "one-row", "stage-edges", "deep", "split-rows"]
 
 
 @pytest.mark.parametrize("layout", ["in_out", "out_in"])
