@@ -14,6 +14,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSlots = 8;  // row loads in flight per thread
 
 __global__ __launch_bounds__(kThreads) void unpermute_kernel(const uint16_t* __restrict__ y_perm,
                                                              const int32_t* __restrict__ inv,
@@ -36,15 +37,26 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const uint16_t* __r
   for (int64_t t = (int64_t)blockIdx.x * rows_per_iter + r_local; t < T; t += (int64_t)gridDim.x * rows_per_iter) {
     for (int64_t ch = ch0; ch < cpr; ch += ch_step) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int64_t p = inv[t * k + j];
-        if (p < 0 || p >= S) continue;
-        const float wt = w != nullptr ? w[t * k + j] : 1.0f;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(y_perm + p * d + ch * 8);
+      // slots in groups of kSlots: all of a group's row loads are issued before any is used
+      for (int j0 = 0; j0 < k; j0 += kSlots) {
+        u32x4 v[kSlots];
+        float wt[kSlots];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(wt, bf16_bits_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(wt, bf16_bits_to_f32(v[q] >> 16), acc[2 * q + 1]);
+        for (int jj = 0; jj < kSlots; ++jj) {
+          const int j = j0 + jj;
+          const int64_t p = j < k ? (int64_t)inv[t * k + j] : -1;
+          const bool keep = p >= 0 && p < S;
+          wt[jj] = keep ? (w != nullptr ? w[t * k + j] : 1.0f) : 0.0f;
+          v[jj] = keep ? *reinterpret_cast<const u32x4*>(y_perm + p * d + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int jj = 0; jj < kSlots; ++jj) {
+          if (j0 + jj >= k) break;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = fmaf(wt[jj], bf16_bits_to_f32(v[jj][q] & 0xFFFFu), acc[2 * q]);
+            acc[2 * q + 1] = fmaf(wt[jj], bf16_bits_to_f32(v[jj][q] >> 16), acc[2 * q + 1]);
+          }
         }
       }
       u32x4 o;
