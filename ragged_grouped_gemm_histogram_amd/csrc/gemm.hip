@@ -423,7 +423,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
       }
     }
     const uint64_t b_step = (uint64_t)(B_NMAJOR ? BK * g.ldw : BK) * 2;
-    auto issue = [&](int kt) {
+    // Loads of stage kt, the ones with index % parts == part (issue(kt) issues them all).
+    auto issue_part = [&](int kt, int part, int parts) {
       const uint32_t sa = lds0 + (uint32_t)((kt % NST) * C::STAGE_BYTES);
       const uint32_t sb = sa + C::A_BYTES;
       const uint64_t ak = a_base + (uint64_t)kt * (BK * 2);
@@ -431,11 +432,12 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
       const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
 #pragma unroll
       for (int t2 = 0; t2 < C::A_OPS; ++t2)
-        dma16_off(ak, a_off[t2], sa + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
+        if (t2 % parts == part) dma16_off(ak, a_off[t2], sa + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
 #pragma unroll
       for (int t2 = 0; t2 < C::B_OPS; ++t2)
-        dma16_off(bk, b_off[t2], sb + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
+        if (t2 % parts == part) dma16_off(bk, b_off[t2], sb + wave_lds + (uint32_t)(C::NWAVES * t2 * 1024));
     };
+    auto issue = [&](int kt) { issue_part(kt, 0, 1); };
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -483,11 +485,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         }
       }
     };
+    // B-fragment-major order: the first MFMAs of a slice need the A fragments (read first) and
+    // one B fragment, so the B reads issued last have the most matrix work to hide behind.
     auto mfmas = [&](int set) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+        for (int i = 0; i < C::FM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
     };
     // Stage kt is complete for this wave once only the later stages already
@@ -514,11 +518,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
     for (int kt = 0; kt < nk; ++kt) {
       // The slot stage kt+NST-1 fills held stage kt-1, which every wave finished
       // reading before the barrier that made stage kt visible.
-      if (kt + NST - 1 < nk) issue(kt + NST - 1);
+      // With a 3-slot ring (128-row tiles) the next stage's loads are spread over the four
+      // slices; the 2-slot ring issues them all at once, a stage ahead.
+      constexpr int kParts = NST >= 3 ? BK / 16 : 1;
+      const bool more = kt + NST - 1 < nk;
       const int slot = kt % NST;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int cur = ks & 1;
+        if (more && ks < kParts) issue_part(kt + NST - 1, ks, kParts);
         if constexpr (!kPrefetch) {
           load_frags(0, slot, ks);
           mfmas(0);
