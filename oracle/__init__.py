@@ -28,7 +28,8 @@ which the method states its accumulation; the test suite pins the two against
 each other within the float32 error bound.
 """
 
-from .backward import grouped_dgrad, grouped_wgrad, permute_backward, unpermute_backward
+from .backward import (expert_backward, grouped_dgrad, grouped_wgrad, permute_backward, swiglu_backward,
+                       unpermute_backward)
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
 from .moe import (
     MoeOracleResult,
@@ -56,6 +57,7 @@ __all__ = [
     "capacity_eq16",
     "entropy_deficit",
     "exclusive_offsets",
+    "expert_backward",
     "expert_forward",
     "f64_to_bf16_bits",
     "grouped_dgrad",
@@ -69,6 +71,7 @@ __all__ = [
     "round_to_bf16",
     "route_histogram",
     "stable_route_order",
+    "swiglu_backward",
     "tile_count",
     "token_forward",
     "unpermute",

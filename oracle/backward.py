@@ -25,6 +25,10 @@ Readings taken where the pages are silent (each is listed in the design notes):
   kept slots (rows of dropped slots do not exist) and the routing-weight
   gradient dw[t, j] = sum_c dy[t, c] * y_perm[inv[t, j], c] in float32, 0 for
   dropped slots.
+* The pages define the projections' backward, not the activation's: the
+  SwiGLU backward here is the derivative of SiLU(g) * up with the forward's
+  bf16 roundings taken as identities, evaluated from the stored bf16 U (which
+  the backward recomputes as the forward projection X_e W_ug[e]^T).
 """
 
 from __future__ import annotations
@@ -140,3 +144,62 @@ def unpermute_backward(dy_bits, y_perm_bits, inv, routing_w, T: int, k: int, M: 
             dyp[col[keep]] = w[keep, j][:, None] * dy[keep]
             dw[keep, j] = np.sum(dy[keep] * yp[col[keep]], axis=1)
     return f64_to_bf16_bits(dyp), dw.astype(np.float32)
+
+
+def swiglu_backward(dh_bits, u_bits) -> np.ndarray:
+    """Backward of H = SiLU(G) * Up with [G | Up] = U (gate block first, as in the forward).
+
+    ``dh_bits`` uint16 [M, h], ``u_bits`` uint16 [M, 2h] (the stored, bf16-rounded
+    pre-activation). With s = sigmoid(g): dG = dH * up * s * (1 + g * (1 - s)),
+    dUp = dH * g * s, evaluated in float64 and rounded to bf16 (the forward's
+    roundings are taken as identities, as autograd takes them). Returns uint16
+    [M, 2h] laid out like U.
+    """
+    dh = bf16_bits_to_f64(np.asarray(dh_bits, dtype=np.uint16))
+    u_all = bf16_bits_to_f64(np.asarray(u_bits, dtype=np.uint16))
+    h = dh.shape[1]
+    if u_all.shape[1] != 2 * h:
+        raise ValueError(f"U must be [M, 2h] with h = {h}, got {u_all.shape}")
+    g, up = u_all[:, :h], u_all[:, h:]
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
+    dg = dh * up * s * (1.0 + g * (1.0 - s))
+    dup = dh * g * s
+    return f64_to_bf16_bits(np.concatenate([dg, dup], axis=1))
+
+
+def expert_backward(dy_bits, x_bits, expert_ids, routing_w, w_ug_bits, w_down_bits):
+    """The expert step's backward, composed from the functions above (test infrastructure only).
+
+    Recomputes the forward (oracle) to get the stored bf16 tensors, then:
+    unpermute backward -> Dgrad/Wgrad of the down projection -> SwiGLU
+    backward -> Dgrad/Wgrad of the gate/up projection -> permute backward.
+    Returns a dict with dx [T, d], d_routing_w [T, k], dw_ug [E, 2h, d],
+    dw_down [E, h, d] (uint16 bf16 bits, float32 for d_routing_w) and the
+    intermediates dy_perm, dh, du, dx_perm.
+    """
+    from .moe import (exclusive_offsets, expert_forward, grouped_projection, permute_rows, route_histogram,
+                      stable_route_order)
+
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    ids = np.asarray(expert_ids)
+    T, k = ids.shape
+    w_ug_bits = np.asarray(w_ug_bits, dtype=np.uint16)
+    w_down_bits = np.asarray(w_down_bits, dtype=np.uint16)
+    E = w_ug_bits.shape[0]
+    counts = route_histogram(ids, E)
+    offsets = exclusive_offsets(counts)
+    M = int(offsets[-1])
+    perm, inv = stable_route_order(ids, E, offsets)
+    x_perm = permute_rows(x_bits, perm, M, k)
+    h_bits, y_perm = expert_forward(x_perm, offsets, w_ug_bits, w_down_bits)
+    u_bits = grouped_projection(x_perm, offsets, np.swapaxes(w_ug_bits, 1, 2))  # U_e = bf16(X_e W_ug[e]^T)
+    dy_perm, d_rw = unpermute_backward(dy_bits, y_perm, inv, routing_w, T, k, M)
+    dh = grouped_dgrad(dy_perm, offsets, w_down_bits, "in_out")
+    dw_down = grouped_wgrad(h_bits, dy_perm, offsets, "in_out")
+    du = swiglu_backward(dh, u_bits)
+    dx_perm = grouped_dgrad(du, offsets, w_ug_bits, "out_in")
+    dw_ug = grouped_wgrad(x_perm, du, offsets, "out_in")
+    dx = permute_backward(dx_perm, inv, T, k)
+    return {"dx": dx, "d_routing_w": d_rw, "dw_ug": dw_ug, "dw_down": dw_down, "dy_perm": dy_perm, "dh": dh,
+            "du": du, "dx_perm": dx_perm, "offsets": offsets, "inv_map": inv.reshape(T, k), "u": u_bits}

@@ -410,6 +410,51 @@ def pin_permutation_backward_is_autograd(orc) -> None:
     np.testing.assert_allclose(dw, wt.grad.detach().numpy().astype(np.float32), rtol=1e-6, atol=1e-6)
 
 
+def pin_swiglu_backward_is_autograd(orc) -> None:
+    """The SwiGLU backward equals torch autograd of F.silu(g) * up in float64 on the bf16 U."""
+    rng = np.random.default_rng(91)
+    M, h = 37, 24
+    u = to_bf16_bits(2.0 * rng.standard_normal((M, 2 * h), dtype=np.float32))
+    dh = to_bf16_bits(rng.standard_normal((M, h), dtype=np.float32))
+    ut = _bits_to_f64(u).requires_grad_(True)
+    hid = F.silu(ut[:, :h]) * ut[:, h:]
+    (hid * _bits_to_f64(dh)).sum().backward()
+    _assert_close_bits(orc.swiglu_backward(dh, u), _torch_bf16_bits(ut.grad.detach()), "SwiGLU backward",
+                       min_exact=0.999, max_ulp=1)
+
+
+def pin_expert_backward_is_autograd(orc) -> None:
+    """The composed expert backward against torch autograd of the whole step in float64 (Eq 13 per
+    expert, gather, weighted scatter-back), rounding points of the forward taken as identities. The
+    oracle rounds U, H, Y and every stored gradient to bf16, so the two agree to bf16 accuracy; a
+    wrong sign, transpose, expert or missing term is off by O(1)."""
+    wl = make_random(T=24, k=2, E=4, d=16, h=12, seed=93, drop_frac=0.15, w_sigma=0.3, empty_experts=(2,))
+    rng = np.random.default_rng(94)
+    dy = to_bf16_bits(rng.standard_normal((wl.T, wl.d), dtype=np.float32))
+    got = orc.expert_backward(dy, wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
+    x = _bits_to_f64(wl.x).requires_grad_(True)
+    wug = _bits_to_f64(wl.w_ug).requires_grad_(True)
+    wdn = _bits_to_f64(wl.w_down).requires_grad_(True)
+    rw = torch.from_numpy(wl.routing_w.astype(np.float64)).requires_grad_(True)
+    y = torch.zeros((wl.T, wl.d), dtype=torch.float64)
+    h = wl.h
+    for t in range(wl.T):
+        for j in range(wl.k):
+            e = int(wl.expert_ids[t, j])
+            if not 0 <= e < wl.E:
+                continue
+            u = x[t] @ wug[e].T
+            y = y.index_add(0, torch.tensor([t]), (rw[t, j] * ((F.silu(u[:h]) * u[h:]) @ wdn[e]))[None])
+    (y * _bits_to_f64(dy)).sum().backward()
+    for name, ref in (("dx", x.grad), ("dw_ug", wug.grad), ("dw_down", wdn.grad)):
+        g = _bits_to_f64(got[name]).numpy()
+        r = ref.detach().numpy()
+        assert np.linalg.norm(g - r) <= 2e-2 * np.linalg.norm(r), f"{name}: rel err {np.linalg.norm(g - r) / np.linalg.norm(r)}"
+    r = rw.grad.detach().numpy()
+    assert np.linalg.norm(got["d_routing_w"] - r) <= 2e-2 * np.linalg.norm(r)
+    assert np.all(_bits_to_f64(got["dw_ug"]).numpy()[2] == 0) and np.all(_bits_to_f64(got["dw_down"]).numpy()[2] == 0)
+
+
 ALL_PINS = [
     pin_toy_golden,
     pin_printed_arithmetic,
@@ -427,4 +472,6 @@ ALL_PINS = [
     pin_backward_is_autograd,
     pin_backward_brute_force,
     pin_permutation_backward_is_autograd,
+    pin_swiglu_backward_is_autograd,
+    pin_expert_backward_is_autograd,
 ]

@@ -139,6 +139,25 @@ def _permute_bwd_first_slot_only(dx_perm_bits, inv, T, k, precision="f64"):
     return _orig_permute_bwd(dx_perm_bits, inv, T, k, precision)
 
 
+_orig_swiglu_bwd = ob.swiglu_backward
+
+
+def _swiglu_bwd_no_sigmoid_term(dh_bits, u_bits):
+    # the sigmoid's own derivative dropped from dG
+    dh = bf16_bits_to_f64(np.asarray(dh_bits, dtype=np.uint16))
+    u_all = bf16_bits_to_f64(np.asarray(u_bits, dtype=np.uint16))
+    h = dh.shape[1]
+    g, up = u_all[:, :h], u_all[:, h:]
+    s = 1.0 / (1.0 + np.exp(-g))
+    return f64_to_bf16_bits(np.concatenate([dh * up * s, dh * g * s], axis=1))
+
+
+def _swiglu_bwd_halves_swapped(dh_bits, u_bits):
+    out = _orig_swiglu_bwd(dh_bits, u_bits)
+    h = out.shape[1] // 2
+    return np.concatenate([out[:, h:], out[:, :h]], axis=1)
+
+
 def _unpermute_bwd_unweighted(dy_bits, y_perm_bits, inv, routing_w, T, k, M):
     return _orig_unpermute_bwd(dy_bits, y_perm_bits, inv, np.ones_like(np.asarray(routing_w)), T, k, M)
 
@@ -163,6 +182,8 @@ MUTATIONS = {
     "wgrad_row_short": [("grouped_wgrad", _wgrad_rows_off_by_one)],
     "permute_backward_one_slot": [("permute_backward", _permute_bwd_first_slot_only)],
     "unpermute_backward_unweighted": [("unpermute_backward", _unpermute_bwd_unweighted)],
+    "swiglu_backward_sigmoid_term_dropped": [("swiglu_backward", _swiglu_bwd_no_sigmoid_term)],
+    "swiglu_backward_halves_swapped": [("swiglu_backward", _swiglu_bwd_halves_swapped)],
 }
 
 
