@@ -189,6 +189,34 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const f
  * ------------------------------------------------------------------------- */
 typedef enum moe_weight_layout { MOE_W_IN_OUT = 0, MOE_W_OUT_IN = 1 } moe_weight_layout;
 
+/* One grouped projection without activation: y[rows_e] = bf16(x[rows_e] * W_e)
+ * (the forward of Eq 15's Y_e = X_e W_e).
+ *
+ *   x        bf16  [cap_rows, d_in]
+ *   offsets  int32 [E+1]
+ *   w        bf16  [E, d_in, d_out] or [E, d_out, d_in] per w_layout
+ *   y        bf16  [cap_rows, d_out] out (rows past M untouched)
+ *
+ * With MOE_W_IN_OUT this is moe_gemm_down; with MOE_W_OUT_IN and W_ug it
+ * recomputes the gate/up pre-activation U = [G | Up] that the SwiGLU backward
+ * needs. */
+moe_status moe_grouped_projection(const uint16_t* x, const int32_t* offsets, const uint16_t* w, int32_t w_layout,
+                                  int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* y,
+                                  hipStream_t stream);
+
+/* SwiGLU backward over the sorted rows [0, offsets[E]) (clamped to cap_rows):
+ * with [g | up] = u[row] and s = sigmoid(g), du[row] = [dG | dUp] where
+ * dG = bf16(dh * up * s * (1 + g * (1 - s))) and dUp = bf16(dh * g * s),
+ * evaluated in fp32 (the pages define the projections' backward, not the
+ * activation's; the forward's bf16 roundings are taken as identities).
+ *
+ *   dh       bf16  [cap_rows, h]
+ *   u        bf16  [cap_rows, 2h]   gate block then up block, as the forward's U
+ *   offsets  int32 [E+1]
+ *   du       bf16  [cap_rows, 2h]   out (rows past M untouched) */
+moe_status moe_swiglu_backward(const uint16_t* dh, const uint16_t* u, const int32_t* offsets, int32_t E,
+                               int64_t cap_rows, int64_t h, uint16_t* du, hipStream_t stream);
+
 /* Dgrad: dx[rows_e] = bf16(dy[rows_e] * W_e^T) for every expert e.
  *
  *   dy       bf16  [cap_rows, d_out]

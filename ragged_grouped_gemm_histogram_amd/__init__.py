@@ -36,6 +36,8 @@ _SIGNATURES = {
     "grouped_swiglu_expert_gather": (ctypes.c_int,
                                      [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_unpermute": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
+    "moe_grouped_projection": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_swiglu_backward": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp]),
     "moe_grouped_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp]),
     "moe_grouped_wgrad_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "moe_grouped_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _sz, _vp]),
@@ -275,6 +277,57 @@ def _w_dims(w: torch.Tensor, layout: str):
     return (E, a, b) if layout == "in_out" else (E, b, a)  # E, d_in, d_out
 
 
+def moe_grouped_projection(x: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor, layout: str = "in_out", *,
+                           y=None) -> torch.Tensor:
+    """Y[rows_e] = bf16(X[rows_e] @ W_e) with W_e [d_in, d_out] stored per ``layout`` (one launch)."""
+    E, d_in, d_out = _w_dims(w, layout)
+    if x.dim() != 2:
+        raise ValueError("x must be [cap_rows, d_in]")
+    cap, dev = x.shape[0], x.device
+    _want(x, "x", torch.bfloat16, (cap, d_in), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w, "w", torch.bfloat16, tuple(w.shape), dev)
+    y = _out(y, "y", torch.bfloat16, (cap, d_out), dev)
+    _check(load_library().moe_grouped_projection(_ptr(x), _ptr(offsets), _ptr(w), W_LAYOUTS[layout], cap, d_in, d_out,
+                                                 E, _ptr(y), _stream(x)), "moe_grouped_projection")
+    return y
+
+
+def moe_swiglu_backward(dh: torch.Tensor, u: torch.Tensor, offsets: torch.Tensor, *, du=None) -> torch.Tensor:
+    """dU = [dG | dUp] of H = SiLU(G) * Up over the sorted rows [0, offsets[E]) (one launch)."""
+    if dh.dim() != 2 or u.dim() != 2 or offsets.dim() != 1:
+        raise ValueError("expected dh [cap, h], u [cap, 2h] and offsets [E+1]")
+    cap, h = dh.shape
+    E = offsets.shape[0] - 1
+    dev = dh.device
+    _want(dh, "dh", torch.bfloat16, (cap, h), dev)
+    _want(u, "u", torch.bfloat16, (cap, 2 * h), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    du = _out(du, "du", torch.bfloat16, (cap, 2 * h), dev)
+    _check(load_library().moe_swiglu_backward(_ptr(dh), _ptr(u), _ptr(offsets), E, cap, h, _ptr(du), _stream(dh)),
+           "moe_swiglu_backward")
+    return du
+
+
+def moe_expert_backward(dy: torch.Tensor, p: "Permuted", routing_w: torch.Tensor, w_ug: torch.Tensor,
+                        w_down: torch.Tensor, h_buf: torch.Tensor, y_perm: torch.Tensor) -> dict:
+    """The expert step's backward from its forward tensors (``p`` must hold x_perm): returns dx,
+    d_routing_w, dw_ug, dw_down. U is recomputed with the gate/up projection; every step is one of the
+    library's calls above."""
+    if p.x_perm is None:
+        raise ValueError("the backward needs the permuted rows: run moe_permute with gather=True")
+    dy_perm, d_rw = moe_unpermute_backward(dy, y_perm, p.inv_map, routing_w)
+    dh = moe_grouped_dgrad(dy_perm, p.offsets, w_down, "in_out")
+    dw_down = moe_grouped_wgrad(h_buf, dy_perm, p.offsets, "in_out")
+    u = moe_grouped_projection(p.x_perm, p.offsets, w_ug, "out_in")
+    du = moe_swiglu_backward(dh, u, p.offsets)
+    dx_perm = moe_grouped_dgrad(du, p.offsets, w_ug, "out_in")
+    dw_ug = moe_grouped_wgrad(p.x_perm, du, p.offsets, "out_in")
+    dx = moe_permute_backward(dx_perm, p.inv_map)
+    return {"dx": dx, "d_routing_w": d_rw, "dw_ug": dw_ug, "dw_down": dw_down, "dy_perm": dy_perm, "dh": dh,
+            "u": u, "du": du, "dx_perm": dx_perm}
+
+
 def moe_grouped_dgrad(dy: torch.Tensor, offsets: torch.Tensor, w: torch.Tensor, layout: str = "in_out", *,
                       dx=None) -> torch.Tensor:
     """dX[rows_e] = bf16(dY[rows_e] @ W_e^T) for the projection Y_e = X_e W_e (one launch)."""
@@ -376,5 +429,6 @@ __all__ = [
     "grouped_swiglu_expert_gather", "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu",
     "moe_gemm_up_swiglu_gather", "moe_permute", "moe_unpermute",
     "permute_workspace_bytes", "W_LAYOUTS", "moe_grouped_dgrad", "moe_grouped_wgrad", "moe_permute_backward", "wgrad_workspace_bytes",
+    "moe_grouped_projection", "moe_swiglu_backward", "moe_expert_backward",
     "moe_unpermute_backward",
 ]

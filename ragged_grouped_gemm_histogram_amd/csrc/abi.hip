@@ -174,6 +174,37 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* inv_map, const f
   return launched(launch_unpermute(y_perm, inv_map, routing_w, T, k, d, y, stream));
 }
 
+moe_status moe_grouped_projection(const uint16_t* x, const int32_t* offsets, const uint16_t* w, int32_t w_layout,
+                                  int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* y,
+                                  hipStream_t stream) {
+  if (w_layout != MOE_W_IN_OUT && w_layout != MOE_W_OUT_IN) return MOE_ERR_BAD_SHAPE;
+  moe_status st = check_gemm_shape(cap_rows, d_in, d_out, E);
+  if (st != MOE_OK) return st;
+  if (missing(x, cap_rows * d_in) || missing(offsets, E + 1) || missing(w, (int64_t)E * d_in * d_out) ||
+      missing(y, cap_rows * d_out))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x, 16) || misaligned(w, 16) || misaligned(y, 16) || misaligned(offsets, 4)) return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(
+      launch_grouped_projection(x, offsets, w, w_layout == MOE_W_OUT_IN, cap_rows, d_in, d_out, E, y, stream));
+}
+
+moe_status moe_swiglu_backward(const uint16_t* dh, const uint16_t* u, const int32_t* offsets, int32_t E,
+                               int64_t cap_rows, int64_t h, uint16_t* du, hipStream_t stream) {
+  if (cap_rows < 0 || cap_rows > kMaxSlots || bad_width(h) || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_BAD_SHAPE;
+  if (missing(dh, cap_rows * h) || missing(u, cap_rows * 2 * h) || missing(offsets, E + 1) ||
+      missing(du, cap_rows * 2 * h))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(dh, 16) || misaligned(u, 16) || misaligned(du, 16) || misaligned(offsets, 4)) return MOE_ERR_MISALIGNED;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_swiglu_backward(dh, u, offsets, E, cap_rows, h, du, stream));
+}
+
 moe_status moe_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, int32_t w_layout,
                              int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
                              hipStream_t stream) {

@@ -57,6 +57,11 @@ hipError_t launch_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, 
                                         const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
                                         uint16_t* h_buf, hipStream_t stream);
 
+hipError_t launch_grouped_projection(const uint16_t* x, const int32_t* offsets, const uint16_t* w, bool w_out_in,
+                                     int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* y,
+                                     hipStream_t stream);
+hipError_t launch_swiglu_backward(const uint16_t* dh, const uint16_t* u, const int32_t* offsets, int32_t E,
+                                  int64_t cap_rows, int64_t h, uint16_t* du, hipStream_t stream);
 hipError_t launch_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, bool w_out_in,
                                 int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
                                 hipStream_t stream);

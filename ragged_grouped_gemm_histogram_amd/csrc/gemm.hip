@@ -1059,6 +1059,20 @@ using WgradTile = Tile<256, 256, 2, 4, 2, false>;
 
 }  // namespace
 
+hipError_t launch_grouped_projection(const uint16_t* x, const int32_t* offsets, const uint16_t* w, bool w_out_in,
+                                     int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* y,
+                                     hipStream_t stream) {
+  // Y_e = X_e W_e: A = x [cap, d_in] (K = d_in), N = d_out, out y [cap, d_out]
+  if (!w_out_in) {
+    // w [E, d_in, d_out]: K rows of N-contiguous columns (the down projection's layout)
+    const GemmArgs g{x, d_in, nullptr, 1, 0, w, d_in * d_out, d_out, 0, d_out, d_in, offsets, E, cap_rows, y, d_out};
+    return launch_grouped<false, true>(g, stream);
+  }
+  // w [E, d_out, d_in]: row n of the operand is W row n, K-contiguous (the gate/up layout, no activation)
+  const GemmArgs g{x, d_in, nullptr, 1, 0, w, d_in * d_out, d_in, 0, d_out, d_in, offsets, E, cap_rows, y, d_out};
+  return launch_grouped<false, false>(g, stream);
+}
+
 hipError_t launch_grouped_dgrad(const uint16_t* dy, const int32_t* offsets, const uint16_t* w, bool w_out_in,
                                 int64_t cap_rows, int64_t d_in, int64_t d_out, int32_t E, uint16_t* dx,
                                 hipStream_t stream) {

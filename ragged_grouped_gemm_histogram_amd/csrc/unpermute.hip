@@ -109,7 +109,59 @@ __global__ __launch_bounds__(kThreads) void unpermute_backward_kernel(
   }
 }
 
+// SwiGLU backward over the sorted rows [0, M), M = offsets[E] clamped to the
+// capacity: with [g | up] = U and s = sigmoid(g) (hardware exponential and
+// reciprocal, fp32), dG = dH * up * s * (1 + g * (1 - s)) and dUp = dH * g * s,
+// each rounded to bf16. Each thread takes 8 consecutive columns of one row.
+__global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(const uint16_t* __restrict__ dh,
+                                                                   const uint16_t* __restrict__ u,
+                                                                   const int32_t* __restrict__ offsets, int E,
+                                                                   int64_t cap_rows, int64_t h,
+                                                                   uint16_t* __restrict__ du) {
+  int64_t M = offsets[E];
+  M = M < 0 ? 0 : (M > cap_rows ? cap_rows : M);
+  const int64_t cpr = h / 8;
+  const int64_t total = M * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = i / cpr, c = (i - r * cpr) * 8;
+    const u32x4 gd = *reinterpret_cast<const u32x4*>(dh + r * h + c);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(u + r * 2 * h + c);
+    const u32x4 uv = *reinterpret_cast<const u32x4*>(u + r * 2 * h + h + c);
+    u32x4 og, ou;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float dg[2], dup[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int sh = 16 * s2;
+        const float d = bf16_bits_to_f32((gd[q] >> sh) & 0xFFFFu);
+        const float g = bf16_bits_to_f32((gv[q] >> sh) & 0xFFFFu);
+        const float up = bf16_bits_to_f32((uv[q] >> sh) & 0xFFFFu);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+        dg[s2] = d * up * sg * (1.0f + g * (1.0f - sg));
+        dup[s2] = d * g * sg;
+      }
+      og[q] = pack_bf16x2(dg[0], dg[1]);
+      ou[q] = pack_bf16x2(dup[0], dup[1]);
+    }
+    *reinterpret_cast<u32x4*>(du + r * 2 * h + c) = og;
+    *reinterpret_cast<u32x4*>(du + r * 2 * h + h + c) = ou;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_backward(const uint16_t* dh, const uint16_t* u, const int32_t* offsets, int32_t E,
+                                  int64_t cap_rows, int64_t h, uint16_t* du, hipStream_t stream) {
+  if (cap_rows == 0) return hipSuccess;
+  const int dev = current_device();
+  int64_t blocks = (cap_rows * (h / 8) + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)device_cu_count(dev) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(swiglu_backward_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, dh, u, offsets, E,
+                     cap_rows, h, du);
+  return hipGetLastError();
+}
 
 hipError_t launch_unpermute_backward(const uint16_t* dy, const uint16_t* y_perm, const int32_t* inv, const float* w,
                                      int64_t T, int32_t k, int64_t d, uint16_t* dy_perm, float* dw,

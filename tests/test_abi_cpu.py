@@ -212,3 +212,19 @@ def test_binding_backward_rejects_bad_layout():
     w = torch.zeros((2, 16, 24), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.moe_grouped_dgrad(torch.zeros((4, 24), dtype=torch.bfloat16), torch.zeros(3, dtype=torch.int32), w, "io")
+
+
+def test_projection_and_swiglu_backward_validation(lib):
+    f = lib.moe_grouped_projection
+    assert f(FAKE, FAKE, FAKE, 3, 16, 16, 24, 2, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 0, 16, 12, 24, 2, FAKE, None) == SHAPE
+    assert f(None, FAKE, FAKE, 0, 16, 16, 24, 2, FAKE, None) == NULLP
+    assert f(FAKE, FAKE, FAKE, 1, 16, 16, 24, 2, FAKE + 8, None) == ALIGN
+    g = lib.moe_swiglu_backward
+    assert g(FAKE, FAKE, FAKE, 2, 16, 12, FAKE, None) == SHAPE
+    assert g(FAKE, FAKE, FAKE, 0, 16, 16, FAKE, None) == SHAPE
+    assert g(FAKE, None, FAKE, 2, 16, 16, FAKE, None) == NULLP
+    assert g(FAKE, FAKE, FAKE, 2, 16, 16, FAKE + 2, None) == ALIGN
+    if not torch.cuda.is_available():
+        assert f(FAKE, FAKE, FAKE, 0, 16, 16, 24, 2, FAKE, None) == DEV
+        assert g(FAKE, FAKE, FAKE, 2, 16, 16, FAKE, None) == DEV
