@@ -13,20 +13,28 @@
  *   moe_unpermute          atomic-free gather + weighted reduction back to
  *                          token order through the inverse map.
  *
+ * The grouped expert also comes as its two single-launch halves and with the
+ * permuted gather fused into the gate/up projection's loads. The backward
+ * (Eq 15) adds grouped Dgrad and Wgrad for either weight layout, a plain
+ * grouped projection, the SwiGLU backward and the atomic-free backward of
+ * both permutations.
+ *
  * Sources: "Section 09: Grouped GEMM" of the OLMo-core MoE report (Eq 13 for
  * the expert, Figs 35-37 and Secs 9.2-9.4 for device-side offsets, fixed
- * capacity buffers and unpadded compute) and the halo toolkit's "Grouped GEMM"
- * notes (dropping ids outside [0, E) before the sort, int32 cumulative
- * offsets, the sentinel-padded inverse map used for an atomic-free
- * scatter-back, gate-then-up weight chunks).
+ * capacity buffers and unpadded compute, Sec 9.5 / Eq 15 / Table 15 for the
+ * backward) and the halo toolkit's "Grouped GEMM" notes (dropping ids outside
+ * [0, E) before the sort, int32 cumulative offsets, the sentinel-padded
+ * inverse map used for an atomic-free scatter-back and permute backward,
+ * gate-then-up weight chunks).
  *
  * Conventions shared by every call
  * --------------------------------
  * - Every tensor pointer is a DEVICE pointer on the current HIP device. bf16
  *   values are passed as uint16_t bit patterns. Every tensor is dense and
  *   row-major with the shape given next to it.
- * - The caller allocates and frees every buffer. The library keeps no state
- *   between calls beyond per-device properties it caches on first use.
+ * - The caller allocates and frees every buffer, workspaces included. The
+ *   library keeps no state between calls beyond per-device properties it
+ *   caches on first use.
  * - Calls are asynchronous on `stream`: no call synchronises, copies a count
  *   to the host or allocates. Row counts exist only as device data.
  * - Shapes are capacity shapes: S = T*k dispatch slots; x_perm, h_buf and

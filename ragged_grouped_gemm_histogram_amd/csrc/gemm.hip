@@ -1,9 +1,13 @@
-// Persistent grouped GEMM over ragged per-expert row blocks, bf16 MFMA with
-// fp32 accumulation, for the two projections of a SwiGLU expert (OLMo report,
-// Eq 13):
+// Persistent grouped GEMMs over ragged per-expert row blocks, bf16 MFMA with
+// fp32 accumulation. The forward's two projections of a SwiGLU expert (OLMo
+// report, Eq 13):
 //
 //   up:   h_buf[rows_e]  = bf16( SiLU(bf16(G)) * bf16(U) ),  [G | U] = x_perm[rows_e] * W_ug[e]^T
 //   down: y_perm[rows_e] = bf16( h_buf[rows_e] * W_down[e] )
+//
+// and, with the same kernels, any plain grouped projection and its input
+// gradient (Eq 15's Dgrad is forward-shaped); the weight gradient, which
+// contracts over the ragged rows, has its own kernel further down.
 //
 // OLMo report Sec 9.2 / Fig 37: the offsets stay on the device; one grouped
 // kernel walks the tiles of every expert's problem. Here each workgroup
@@ -11,29 +15,31 @@
 // sorted rows [offsets[e], offsets[e+1]); its pointers are affine in e and
 // offsets[e]), then takes output tiles in a static round-robin until none is
 // left. Empty experts contribute no tile; rows past an expert's block and
-// columns past N are never stored.
+// columns past N are never stored. The A rows of the up projection can be
+// gathered from the token matrix through the dispatch order instead of a
+// permuted copy.
 //
-// Tile: BM rows x BN weight rows, K stepped by 64. 4 waves in a 2x2 grid, each
-// owning (BM/2) x (BN/2) outputs as 32x32 blocks of v_mfma_f32_32x32x16_bf16.
-// The MFMA takes the weight fragment as its first operand, so each lane ends
-// up holding four consecutive output columns of one output row; the epilogue
-// packs them to bf16, stages the tile through LDS and writes 16-byte chunks.
+// Tiles are 32x32 blocks of v_mfma_f32_32x32x16_bf16 per wave. The MFMA takes
+// the weight fragment as its first operand, so each lane ends up holding four
+// consecutive output columns of one output row; the epilogue packs them to
+// bf16, stages the tile through LDS and writes 16-byte chunks. For the up
+// projection the BN weight rows of a tile are BN/2 gate rows followed by the
+// BN/2 matching up rows (W_ug is gate-then-up, chunked), so a lane holds each
+// gate value and its up value in the same register slot and SwiGLU is applied
+// in registers.
 //
-// For the up projection the BN weight rows of a tile are BN/2 gate rows
-// followed by the BN/2 matching up rows (W_ug is gate-then-up, chunked), so a
-// lane holds each gate value and its up value in the same register slot and
-// SwiGLU is applied in registers.
-//
-// Two main loops share that structure:
-//  * pipelined (K % 64 == 0, every realistic width): global -> LDS direct
-//    loads (global_load_lds_dwordx4) into a 3-stage ring, two stages in flight
-//    while the third feeds the MFMAs, one barrier per K step, no staging
-//    registers. W_down [h, d] is N-contiguous; its tiles land in LDS as they
-//    are in memory and the MFMA fragments are read with the gfx950 LDS
-//    transpose read (ds_read_b64_tr_b16).
+// Two main loops:
+//  * pipelined (K % 64 == 0): global -> LDS direct loads
+//    (global_load_lds_dwordx4) into a ring of 64-deep stages, one barrier per
+//    stage, the next 16-deep slice's fragments read under the current slice's
+//    MFMAs; 256 x 256 tiles on 8 waves with a 2-slot ring for large expert
+//    blocks, 128 x 256 tiles on 8 waves with a 3-slot ring otherwise.
+//    N-contiguous weights (W_down [h, d]) land in LDS as they are in memory
+//    and their fragments come from the gfx950 LDS transpose read
+//    (ds_read_b64_tr_b16).
 //  * register-staged (any K % 8 == 0): global -> registers -> LDS with zero
-//    fill for the K remainder, double-buffered; W_down blocks of 8(k) x 8(n)
-//    are transposed in registers.
+//    fill for the K remainder, double-buffered, 128 x 256 tiles on 4 waves;
+//    N-contiguous blocks of 8(k) x 8(n) are transposed in registers.
 
 #include "common.h"
 
