@@ -188,6 +188,9 @@ def main(argv=None):
     value = flops / (ms_per_step * 1e-3) / 1e12
     names = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
     stage_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
+    step_ev = sorted(ev[0].elapsed_time(ev[4]) for ev in events)  # each step's own span on the stream
+    step_events = {"mean_ms": sum(step_ev) / len(step_ev), "median_ms": step_ev[len(step_ev) // 2],
+                   "min_ms": step_ev[0], "max_ms": step_ev[-1]}
     algo = algorithmic_bytes(T, k, M, d, h, nonempty, fused)
     gemm1_flops = 2 * M * d * (2 * h)
     gemm2_flops = 2 * M * h * d
@@ -250,6 +253,7 @@ def main(argv=None):
                    "seed": WORKLOADS[wl.name][0], "parallelism": "single GPU",
                    "gather": "fused into the gate/up GEMM" if fused else "x_perm copy in moe_permute"},
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "step_events": step_events,
         "useful_gflop": flops / 1e9,
         "stages": stages,
         "roofline": roofline,
