@@ -2,12 +2,15 @@
 """Throughput of the routed MoE expert step (permute + grouped SwiGLU expert + unpermute) on one MI355X.
 
 Metric: useful TFLOP/s = 6 * sum_e M_e * d * h / t, where t is the wall time of
-one whole step (moe_permute, grouped_swiglu_expert, moe_unpermute) on one
+one whole step (moe_permute, the grouped SwiGLU expert, moe_unpermute) on one
 stream with inputs resident in HBM; also reported as a share of the dense bf16
 MFMA peak. The useful-FLOP convention (two FLOPs per multiply-add, three
 projections of d x h per gated expert, nothing for the activation, routing or
 permutations) is the grouped-expert essay's; the timing protocol (warm-up
 steps, then a fixed number of queued steps) follows the OLMo report's Fig 38.
+The step is timed twice: K eager steps with HIP events around every stage (the
+per-stage times and the roofline come from these), then K replays of the same
+step captured once in a HIP graph, which is the headline unless --eager.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config zipf64]
 Prints one JSON line. Extra measurements ride along in the same line:
@@ -101,6 +104,8 @@ def main(argv=None):
                     help="copy rows into x_perm in moe_permute instead of gathering them inside the gate/up GEMM")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="report eager launches as the headline instead of replays of the step captured in a HIP graph")
     ap.add_argument("--sweep", choices=SWEEPS,
                     help="instead of the step, run one sweep and print its own JSON line: histogram (Fig 40), "
                          "capacity (Fig 38) or decomposition (Fig 39) of one grouped projection, or the step's "
@@ -181,9 +186,35 @@ def main(argv=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    eager_ms = elapsed * 1e3 / args.steps
+    graph_ms, graph_note = None, None
+    if not args.eager:
+        # The same step captured once in a HIP graph (the library allocates, synchronises and copies
+        # nothing, so its calls capture as they are), then exactly K replays timed like the eager
+        # steps: the kernels are identical, the host launch gaps between them are gone.
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    step()
+            torch.cuda.current_stream().wait_stream(side)
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            tg = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+        except Exception as exc:  # capture unavailable: the eager time stays the headline
+            graph_note = f"graph capture failed ({type(exc).__name__}: {exc}); eager launches reported"
+            torch.cuda.synchronize()
+
     M = int(offsets[-1].item())
     nonempty = int((counts > 0).sum().item())
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
     flops = useful_flops(M, d, h)
     value = flops / (ms_per_step * 1e-3) / 1e12
     names = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
@@ -253,6 +284,9 @@ def main(argv=None):
                    "seed": WORKLOADS[wl.name][0], "parallelism": "single GPU",
                    "gather": "fused into the gate/up GEMM" if fused else "x_perm copy in moe_permute"},
         "pct_of_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "timing": "replays of the step captured in a HIP graph" if graph_ms is not None else "eager launches",
+        "eager_ms_per_step": eager_ms,
+        "graph_note": graph_note,
         "step_events": step_events,
         "useful_gflop": flops / 1e9,
         "stages": stages,
