@@ -525,14 +525,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
       // The slot stage kt+NST-1 fills held stage kt-1, which every wave finished
       // reading before the barrier that made stage kt visible.
       // With a 3-slot ring (128-row tiles) the next stage's loads are spread over the four
-      // slices; the 2-slot ring issues them all at once, a stage ahead.
+      // slices; the 2-slot ring issues them all at once, a stage ahead (with fragment
+      // prefetch, right after that barrier, inside the previous stage's last slice).
       constexpr int kParts = NST >= 3 ? BK / 16 : 1;
       const bool more = kt + NST - 1 < nk;
       const int slot = kt % NST;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int cur = ks & 1;
-        if (more && ks < kParts) issue_part(kt + NST - 1, ks, kParts);
+        if (more && ks < kParts && (!kPrefetch || NST > 2 || kt == 0)) issue_part(kt + NST - 1, ks, kParts);
         if constexpr (!kPrefetch) {
           load_frags(0, slot, ks);
           mfmas(0);
@@ -542,11 +543,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
           mfmas(cur);
           interleave_reads<C::FM * C::FN, C::FM + (B_NMAJOR ? 2 : 1) * C::FN>();
         } else {
-          mfmas(cur);
+          // The last slice's fragments are already in registers: hand the stage
+          // off first (wait, barrier, refill of the slot just drained, reads of
+          // the next stage's first slice) so that its MFMAs cover the barrier
+          // and the read latency. The MFMAs stay outside the branch so the
+          // accumulators keep one register assignment.
           if (kt + 1 < nk) {
             wait_stage(kt + 1);
-            load_frags(0, (kt + 1) % NST, 0);
+            if (NST == 2 && kt + 2 < nk) issue(kt + 2);
+            load_frags(cur ^ 1, (kt + 1) % NST, 0);
           }
+          mfmas(cur);
         }
       }
     }
