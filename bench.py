@@ -587,7 +587,8 @@ def sweep_backward(torch, moe, dev, warmup, samples):
     pre-activation U, SwiGLU backward, Dgrad and Wgrad of the gate/up projection ([E, 2h, d]) and the
     permute backward, each timed on its own (queued samples, HIP events). ``value`` is the useful
     backward work, 12*M*d*h (the four backward GEMMs, 2*M*d_in*d_out each), over the summed time of
-    every kernel of the chain, the U recompute included."""
+    every kernel of the chain, the U recompute included. ``with_saved_u`` gives the chain without the
+    recompute, and what keeping U costs the forward's gate/up launch (moe_gemm_up_swiglu_u)."""
     import numpy as np
 
     from workloads import make_workload
@@ -647,12 +648,27 @@ def sweep_backward(torch, moe, dev, warmup, samples):
         total_ms += r["mean_ms"]
         res[name] = entry
         _progress(f"backward: {name} {r['mean_ms']:.4f} ms")
+    # A forward that keeps U (moe_gemm_up_swiglu_u) lets the backward drop the recompute; the
+    # forward's gate/up launch pays for the extra U stores instead.
+    h2 = torch.empty_like(h_buf)
+    fwd = {}
+    for name, fn in (("gate_up", lambda: moe.moe_gemm_up_swiglu(p.x_perm, p.offsets, w_ug, h_buf=h2)),
+                     ("gate_up_save_u", lambda: moe.moe_gemm_up_swiglu_u(p.x_perm, p.offsets, w_ug, h_buf=h2,
+                                                                          u_buf=u))):
+        r = timer(fn, warmup, samples)
+        fwd[name] = {"ms": r["mean_ms"], "TFLOP/s": 4 * M * h * d / r["mean_ms"] / 1e9}
+        _progress(f"backward: forward {name} {r['mean_ms']:.4f} ms")
+    saved_ms = total_ms - res["recompute_u"]["ms"]
     return {"metric": "useful TFLOP/s of the expert step's backward (12*M*d*h over every kernel of the chain)",
             "sweep": "backward", "value": gemm_flops / total_ms / 1e9, "unit": "TFLOP/s", "data": "synthetic",
             "dtype": "bf16",
             "config": {"workload": "zipf64 backward", "T": T, "k": k, "E": E, "d": d, "h": h, "M": M,
                        "warmup": warmup, "samples": samples},
-            "backward_ms": total_ms, "stages": res, "gate_overruns": timer.gate_overruns}
+            "backward_ms": total_ms, "stages": res,
+            "with_saved_u": {"backward_ms": saved_ms, "TFLOP/s": gemm_flops / saved_ms / 1e9,
+                             "forward_gate_up": fwd,
+                             "forward_extra_ms": fwd["gate_up_save_u"]["ms"] - fwd["gate_up"]["ms"]},
+            "gate_overruns": timer.gate_overruns}
 
 
 SWEEPS = {"histogram": sweep_histogram, "capacity": sweep_capacity, "decomposition": sweep_decomposition,

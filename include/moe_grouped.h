@@ -16,8 +16,9 @@
  * The grouped expert also comes as its two single-launch halves and with the
  * permuted gather fused into the gate/up projection's loads. The backward
  * (Eq 15) adds grouped Dgrad and Wgrad for either weight layout, a plain
- * grouped projection, the SwiGLU backward and the atomic-free backward of
- * both permutations.
+ * grouped projection, the SwiGLU backward, the atomic-free backward of both
+ * permutations and a gate/up launch that also keeps the pre-activation U for
+ * the backward.
  *
  * Sources: "Section 09: Grouped GEMM" of the OLMo-core MoE report (Eq 13 for
  * the expert, Figs 35-37 and Secs 9.2-9.4 for device-side offsets, fixed
@@ -136,6 +137,23 @@ moe_status grouped_swiglu_expert(const uint16_t* x_perm, const int32_t* offsets,
 moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
                               int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
                               hipStream_t stream);
+
+/* The first half for a forward that keeps what its backward needs: as
+ * moe_gemm_up_swiglu, and the same launch also stores the gate/up
+ * pre-activation of Eq 13,
+ *
+ *   u_buf    bf16  [cap_rows, 2h]  out: u_buf[p] = bf16(x_perm[p] W_ug[e]^T),
+ *                                  gate block (columns [0, h)) then up block
+ *
+ * the bf16 values the SwiGLU epilogue reads (rows past M untouched). The
+ * SwiGLU backward needs U; with u_buf kept, the backward does not recompute
+ * the gate/up projection (OLMo report Sec 9.5, Eq 15: the backward is two more
+ * grouped problems per projection; recomputing U would add a third). h_buf is
+ * bit for bit that of moe_gemm_up_swiglu, u_buf that of
+ * moe_grouped_projection(x_perm, offsets, w_ug, MOE_W_OUT_IN, ...). */
+moe_status moe_gemm_up_swiglu_u(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
+                                uint16_t* u_buf, hipStream_t stream);
 
 /* The first half with the permuted gather fused into its loads (OLMo report
  * Sec 9.4: the up/gate projection reads the dispatch buffer directly instead

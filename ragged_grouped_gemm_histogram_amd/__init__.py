@@ -31,6 +31,7 @@ _SIGNATURES = {
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "grouped_swiglu_expert": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_gemm_up_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
+    "moe_gemm_up_swiglu_u": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_gemm_down": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "moe_gemm_up_swiglu_gather": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
     "grouped_swiglu_expert_gather": (ctypes.c_int,
@@ -179,6 +180,23 @@ def moe_gemm_up_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.
     return h_buf
 
 
+def moe_gemm_up_swiglu_u(x_perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.Tensor, *, h_buf=None,
+                         u_buf=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """moe_gemm_up_swiglu that also stores the pre-activation u_buf = [G | U] = bf16(x_perm[rows_e] @ W_ug[e]^T)
+    ([cap, 2h], gate block first) for the backward; returns (h_buf, u_buf). One launch."""
+    cap, dev = _gemm_shapes(x_perm, offsets, w_ug)
+    E, two_h, d = w_ug.shape
+    h = two_h // 2
+    _want(x_perm, "x_perm", torch.bfloat16, (cap, d), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(w_ug, "w_ug", torch.bfloat16, (E, 2 * h, d), dev)
+    h_buf = _out(h_buf, "h_buf", torch.bfloat16, (cap, h), dev)
+    u_buf = _out(u_buf, "u_buf", torch.bfloat16, (cap, 2 * h), dev)
+    _check(load_library().moe_gemm_up_swiglu_u(_ptr(x_perm), _ptr(offsets), _ptr(w_ug), cap, d, h, E, _ptr(h_buf),
+                                               _ptr(u_buf), _stream(x_perm)), "moe_gemm_up_swiglu_u")
+    return h_buf, u_buf
+
+
 def moe_gemm_up_swiglu_gather(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, w_ug: torch.Tensor,
                               k: int, *, h_buf=None) -> torch.Tensor:
     """moe_gemm_up_swiglu on token rows gathered through perm: sorted row p reads x[perm[p] // k] (one launch)."""
@@ -310,16 +328,18 @@ def moe_swiglu_backward(dh: torch.Tensor, u: torch.Tensor, offsets: torch.Tensor
 
 
 def moe_expert_backward(dy: torch.Tensor, p: "Permuted", routing_w: torch.Tensor, w_ug: torch.Tensor,
-                        w_down: torch.Tensor, h_buf: torch.Tensor, y_perm: torch.Tensor) -> dict:
+                        w_down: torch.Tensor, h_buf: torch.Tensor, y_perm: torch.Tensor, u: torch.Tensor | None = None
+                        ) -> dict:
     """The expert step's backward from its forward tensors (``p`` must hold x_perm): returns dx,
-    d_routing_w, dw_ug, dw_down. U is recomputed with the gate/up projection; every step is one of the
-    library's calls above."""
+    d_routing_w, dw_ug, dw_down. ``u`` is the pre-activation kept by moe_gemm_up_swiglu_u; without it, U is
+    recomputed with the gate/up projection. Every step is one of the library's calls above."""
     if p.x_perm is None:
         raise ValueError("the backward needs the permuted rows: run moe_permute with gather=True")
     dy_perm, d_rw = moe_unpermute_backward(dy, y_perm, p.inv_map, routing_w)
     dh = moe_grouped_dgrad(dy_perm, p.offsets, w_down, "in_out")
     dw_down = moe_grouped_wgrad(h_buf, dy_perm, p.offsets, "in_out")
-    u = moe_grouped_projection(p.x_perm, p.offsets, w_ug, "out_in")
+    if u is None:
+        u = moe_grouped_projection(p.x_perm, p.offsets, w_ug, "out_in")
     du = moe_swiglu_backward(dh, u, p.offsets)
     dx_perm = moe_grouped_dgrad(du, p.offsets, w_ug, "out_in")
     dw_ug = moe_grouped_wgrad(p.x_perm, du, p.offsets, "out_in")
@@ -427,7 +447,7 @@ def moe_expert_forward(x, expert_ids, routing_w, w_ug, w_down, fused_gather: boo
 __all__ = [
     "LIB_PATH", "MAX_EXPERTS", "MoeError", "Permuted", "grouped_swiglu_expert", "header_functions", "load_library",
     "grouped_swiglu_expert_gather", "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu",
-    "moe_gemm_up_swiglu_gather", "moe_permute", "moe_unpermute",
+    "moe_gemm_up_swiglu_gather", "moe_gemm_up_swiglu_u", "moe_permute", "moe_unpermute",
     "permute_workspace_bytes", "W_LAYOUTS", "moe_grouped_dgrad", "moe_grouped_wgrad", "moe_permute_backward", "wgrad_workspace_bytes",
     "moe_grouped_projection", "moe_swiglu_backward", "moe_expert_backward",
     "moe_unpermute_backward",

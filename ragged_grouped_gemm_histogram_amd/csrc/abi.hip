@@ -98,6 +98,23 @@ moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, co
   return launched(launch_gemm_up_swiglu(x_perm, offsets, w_ug, cap_rows, d, h, E, h_buf, stream));
 }
 
+moe_status moe_gemm_up_swiglu_u(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf, uint16_t* u_buf,
+                                hipStream_t stream) {
+  moe_status st = check_gemm_shape(cap_rows, d, h, E);
+  if (st != MOE_OK) return st;
+  if (missing(x_perm, cap_rows * d) || missing(offsets, E + 1) || missing(w_ug, (int64_t)E * 2 * h * d) ||
+      missing(h_buf, cap_rows * h) || missing(u_buf, cap_rows * 2 * h))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x_perm, 16) || misaligned(w_ug, 16) || misaligned(h_buf, 16) || misaligned(u_buf, 16) ||
+      misaligned(offsets, 4))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_device()) != MOE_OK) return st;
+  if (cap_rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return launched(launch_gemm_up_swiglu_u(x_perm, offsets, w_ug, cap_rows, d, h, E, h_buf, u_buf, stream));
+}
+
 moe_status moe_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
                                      const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
                                      uint16_t* h_buf, hipStream_t stream) {

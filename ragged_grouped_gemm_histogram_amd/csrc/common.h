@@ -53,6 +53,10 @@ hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets,
                                  int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
                                  hipStream_t stream);
 
+hipError_t launch_gemm_up_swiglu_u(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                   int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
+                                   uint16_t* u_buf, hipStream_t stream);
+
 hipError_t launch_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,
                                         const int32_t* offsets, const uint16_t* w_ug, int64_t d, int64_t h, int32_t E,
                                         uint16_t* h_buf, hipStream_t stream);

@@ -7,7 +7,8 @@
 //
 // and, with the same kernels, any plain grouped projection and its input
 // gradient (Eq 15's Dgrad is forward-shaped); the weight gradient, which
-// contracts over the ragged rows, has its own kernel further down.
+// contracts over the ragged rows, has its own kernel further down. The up
+// projection can also store its bf16 pre-activation [G | U] for the backward.
 //
 // OLMo report Sec 9.2 / Fig 37: the offsets stay on the device; one grouped
 // kernel walks the tiles of every expert's problem. Here each workgroup
@@ -94,6 +95,7 @@ struct GemmArgs {
   int64_t cap_rows;
   uint16_t* out;            // [cap_rows, N], row pitch ldo
   int64_t ldo;
+  uint16_t* u_out = nullptr;  // gated only, optional: the pre-activation U = [G | Up], [cap_rows, 2N], pitch 2N
 };
 
 template <int THREADS>
@@ -267,6 +269,23 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int 
   return c;
 }
 
+// weight-tile row of a wave's fn-th 32-row block (gated: the first FN/2 blocks are gate rows,
+// the rest the matching up rows, BN/2 further down)
+template <class C>
+__device__ __forceinline__ int b_block_row(int wn, int fn) {
+  if constexpr (C::GATED) {
+    constexpr int half_fn = C::FN / 2;
+    const int half = fn / half_fn, sub = fn % half_fn;
+    return half * (C::BN / 2) + wn * (C::BN / 2 / C::WGN) + sub * 32;
+  } else {
+    return wn * C::WTN + fn * 32;
+  }
+}
+
+// SiLU(g) * u of the bf16-rounded gate and up values, in fp32 with the hardware
+// exponential and reciprocal (a few fp32 ulps, far below the bf16 rounding of the result).
+__device__ __forceinline__ float swiglu(float gv, float uv) { return gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv; }
+
 // Registers -> bf16 tile in LDS (swizzled 16-byte chunks) -> global. For the
 // gated projection, SwiGLU is applied here: g and u are rounded to bf16 first,
 // then SiLU(g) * u is evaluated in fp32 with the hardware exponential and
@@ -296,7 +315,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
           for (int s = 0; s < 4; ++s) {
             const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][4 * q + s]));
             const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + half_fn][4 * q + s]));
-            hv[s] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            hv[s] = swiglu(gv, uv);
           }
           const int col = wn * (BN / 2 / C::WGN) + j * 32 + 8 * q + 4 * half_lane;
           const int c = col >> 3;
@@ -337,23 +356,69 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
   lds_barrier();  // LDS is reused by the next tile
 }
 
-// weight-tile row of a wave's fn-th 32-row block (gated: the first FN/2 blocks are gate rows,
-// the rest the matching up rows, BN/2 further down)
+// Gated epilogue that also stores the pre-activation U = [G | Up] ([cap, 2N], pitch 2N). The
+// bf16 U tile (BN/2 gate columns, then the BN/2 matching up columns) is staged in LDS; then each
+// thread takes a gate chunk and its up chunk (8 columns each), stores both to U and the 8 SwiGLU
+// values (the same rounding and arithmetic as the plain epilogue) to the output, so the
+// accumulators are dead once the tile is staged.
 template <class C>
-__device__ __forceinline__ int b_block_row(int wn, int fn) {
-  if constexpr (C::GATED) {
-    constexpr int half_fn = C::FN / 2;
-    const int half = fn / half_fn, sub = fn % half_fn;
-    return half * (C::BN / 2) + wn * (C::BN / 2 / C::WGN) + sub * 32;
-  } else {
-    return wn * C::WTN + fn * 32;
+__device__ __forceinline__ void epilogue_save_u(const f32x16 (&acc)[C::FM][C::FN], unsigned char* smem,
+                                                const GemmArgs& g, const TileCoord& tc) {
+  static_assert(C::GATED, "U exists for the gated projection only");
+  constexpr int BM = C::BM, BN = C::BN;
+  constexpr int U_CPR = BN / 8, U_ROW_BYTES = BN * 2, HALF = U_CPR / 2;
+  static_assert(BM * U_ROW_BYTES <= C::LDS_BYTES, "U tile must fit in the stage buffers");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int half_lane = lane >> 5;
+  unsigned char* ut = smem;  // [BM][BN] bf16
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int r = wm * C::WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = b_block_row<C>(wn, j) + 8 * q + 4 * half_lane;
+        const int c = col >> 3;
+        uint2 pk{pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
+                 pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+        *reinterpret_cast<uint2*>(ut + r * U_ROW_BYTES + ((c ^ (r & (U_CPR - 1))) * 16) + (col & 7) * 2) = pk;
+      }
+    }
   }
+  lds_barrier();
+  const int64_t ldu = 2 * g.N;
+  constexpr int kIters = BM * HALF / C::THREADS;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int idx = it * C::THREADS + tid;
+    const int r = idx / HALF, c = idx % HALF;
+    const int64_t col = tc.n0 + c * 8;
+    if (r < tc.rows_valid && col < g.N) {
+      const u32x4 gu = *reinterpret_cast<const u32x4*>(ut + r * U_ROW_BYTES + ((c ^ (r & (U_CPR - 1))) * 16));
+      const u32x4 uu =
+          *reinterpret_cast<const u32x4*>(ut + r * U_ROW_BYTES + (((c + HALF) ^ (r & (U_CPR - 1))) * 16));
+      uint16_t* urow = g.u_out + (tc.row0 + r) * ldu;
+      *reinterpret_cast<u32x4*>(urow + col) = gu;
+      *reinterpret_cast<u32x4*>(urow + g.N + col) = uu;
+      u32x4 hv;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float h0 = swiglu(bf16_bits_to_f32(gu[w] & 0xFFFFu), bf16_bits_to_f32(uu[w] & 0xFFFFu));
+        const float h1 = swiglu(bf16_bits_to_f32(gu[w] >> 16), bf16_bits_to_f32(uu[w] >> 16));
+        hv[w] = pack_bf16x2(h0, h1);
+      }
+      *reinterpret_cast<u32x4*>(g.out + (tc.row0 + r) * g.ldo + col) = hv;
+    }
+  }
+  lds_barrier();  // LDS is reused by the next tile
 }
 
 // ============================================================================
 // Pipelined main loop: direct global -> LDS loads into an NST-stage ring.
 // ============================================================================
-template <class C, bool B_NMAJOR>
+template <class C, bool B_NMAJOR, bool SAVE_U>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs g) {
   constexpr int BN = C::BN, NST = C::NST;
   constexpr int OPS = C::A_OPS + C::B_OPS;
@@ -558,14 +623,15 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
       }
     }
     lds_barrier();  // every wave is done with the ring (all its loads were waited for) before the epilogue reuses it
-    epilogue<C>(acc, smem, g, tc);
+    if constexpr (SAVE_U) epilogue_save_u<C>(acc, smem, g, tc);
+    else epilogue<C>(acc, smem, g, tc);
   }
 }
 
 // ============================================================================
 // Register-staged main loop: any K % 8 == 0 (zero fill of the K remainder).
 // ============================================================================
-template <class C, bool B_NMAJOR>
+template <class C, bool B_NMAJOR, bool SAVE_U>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs g) {
   constexpr int BN = C::BN;
   static_assert(C::NST == 2, "register-staged loop double-buffers");
@@ -715,7 +781,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs 
       if (kt + 1 < nk) store_stage(buf ^ 1);
       __syncthreads();
     }
-    epilogue<C>(acc, smem, g, tc);
+    if constexpr (SAVE_U) epilogue_save_u<C>(acc, smem, g, tc);
+    else epilogue<C>(acc, smem, g, tc);
   }
 }
 
@@ -1054,18 +1121,19 @@ inline bool offsets_fit_32(const GemmArgs& g) {
   return a_span <= kMax && g.w_expert_stride * 2 <= kMax;
 }
 
-template <bool GATED, bool B_NMAJOR>
+template <bool GATED, bool B_NMAJOR, bool SAVE_U = false>
 hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
   if (g.K % BK == 0 && offsets_fit_32(g)) {
     if (g.cap_rows >= (int64_t)384 * g.E) {
       static bool done[64] = {};
-      return launch_kernel<BigTile<GATED>>(grouped_gemm_pipe_kernel<BigTile<GATED>, B_NMAJOR>, done, g, stream);
+      return launch_kernel<BigTile<GATED>>(grouped_gemm_pipe_kernel<BigTile<GATED>, B_NMAJOR, SAVE_U>, done, g, stream);
     }
     static bool done[64] = {};
-    return launch_kernel<SmallTile<GATED>>(grouped_gemm_pipe_kernel<SmallTile<GATED>, B_NMAJOR>, done, g, stream);
+    return launch_kernel<SmallTile<GATED>>(grouped_gemm_pipe_kernel<SmallTile<GATED>, B_NMAJOR, SAVE_U>, done, g,
+                                           stream);
   }
   static bool done[64] = {};
-  return launch_kernel<RegsTile<GATED>>(grouped_gemm_regs_kernel<RegsTile<GATED>, B_NMAJOR>, done, g, stream);
+  return launch_kernel<RegsTile<GATED>>(grouped_gemm_regs_kernel<RegsTile<GATED>, B_NMAJOR, SAVE_U>, done, g, stream);
 }
 
 using WgradTile = Tile<256, 256, 2, 4, 2, false>;
@@ -1137,6 +1205,15 @@ hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets,
   // A = x_perm [cap, d] (K = d); weights [E, 2h, d], gate rows n, up rows h + n; out h_buf [cap, h]
   const GemmArgs g{x_perm, d, nullptr, 1, 0, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h};
   return launch_grouped<true, false>(g, stream);
+}
+
+hipError_t launch_gemm_up_swiglu_u(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
+                                   int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
+                                   uint16_t* u_buf, hipStream_t stream) {
+  // as launch_gemm_up_swiglu, and the epilogue also stores U [cap, 2h]
+  GemmArgs g{x_perm, d, nullptr, 1, 0, w_ug, 2 * h * d, d, h, h, d, offsets, E, cap_rows, h_buf, h};
+  g.u_out = u_buf;
+  return launch_grouped<true, false, true>(g, stream);
 }
 
 hipError_t launch_gemm_up_swiglu_gather(const uint16_t* x, const int32_t* perm, int64_t T, int32_t k,

@@ -97,6 +97,22 @@ def test_gather_gemm_validation(lib, kw, status):
                                          a["E"], a["out"], None) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(cap=-1), SHAPE), (dict(d=4), SHAPE), (dict(h=20), SHAPE), (dict(E=0), SHAPE),
+    (dict(a=None), NULLP), (dict(offs=None), NULLP), (dict(w=None), NULLP), (dict(out=None), NULLP),
+    (dict(u=None), NULLP), (dict(u=FAKE + 8), ALIGN), (dict(out=FAKE + 2), ALIGN), (dict(offs=FAKE + 2), ALIGN),
+])
+def test_save_u_gemm_validation(lib, kw, status):
+    a = dict(a=FAKE, offs=FAKE, w=FAKE, cap=16, d=16, h=16, E=2, out=FAKE, u=FAKE)
+    a.update(kw)
+    assert lib.moe_gemm_up_swiglu_u(a["a"], a["offs"], a["w"], a["cap"], a["d"], a["h"], a["E"], a["out"], a["u"],
+                                    None) == status
+    if not torch.cuda.is_available():
+        assert lib.moe_gemm_up_swiglu_u(FAKE, FAKE, FAKE, 16, 16, 16, 2, FAKE, FAKE, None) == DEV
+    # an empty capacity needs no row buffers
+    assert lib.moe_gemm_up_swiglu_u(None, FAKE, FAKE, 0, 16, 16, 2, None, None, None) in (OK, DEV)
+
+
 def test_permute_without_gather_needs_no_rows(lib):
     # x_perm = NULL: no row copy, so x may be NULL too; everything else is still required
     assert permute(lib, x=None, xp=None) in (OK, DEV)
