@@ -76,3 +76,73 @@ def test_forward_step_graph_replays(name):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                r.view(torch.int16) if r.dtype == torch.bfloat16 else r), f"replay {rep}: {key} differs"
         say(f"  replay {rep} matches the eager step")
+
+
+def _train_buffers(wl, dev):
+    S, T, k, d, h, E = wl.T * wl.k, wl.T, wl.k, wl.d, wl.h, wl.E
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    b = _buffers(wl, dev)
+    b.update(
+        x_perm=torch.empty((S, d), **bf), u=torch.empty((S, 2 * h), **bf), dy_perm=torch.empty((S, d), **bf),
+        d_rw=torch.empty((T, k), dtype=torch.float32, device=dev), dh=torch.empty((S, h), **bf),
+        du=torch.empty((S, 2 * h), **bf), dx_perm=torch.empty((S, d), **bf), dx=torch.empty((T, d), **bf),
+        dw_down=torch.empty((E, h, d), **bf), dw_ug=torch.empty((E, 2 * h, d), **bf),
+        wws=torch.empty((max(moe.wgrad_workspace_bytes(S, d, 2 * h, E), moe.wgrad_workspace_bytes(S, h, d, E), 16),),
+                        dtype=torch.uint8, device=dev),
+    )
+    return b
+
+
+def _train_step(di, b, dy):
+    """Forward keeping U, then the backward from it: every call writes into b."""
+    p = moe.moe_permute(di.x, di.ids, di.w_ug.shape[0], x_perm=b["x_perm"], counts=b["counts"], offsets=b["offsets"],
+                        perm=b["perm"], inv_map=b["inv"], workspace=b["ws"], gather=True)
+    moe.moe_gemm_up_swiglu_u(p.x_perm, p.offsets, di.w_ug, h_buf=b["h_buf"], u_buf=b["u"])
+    moe.moe_gemm_down(b["h_buf"], p.offsets, di.w_down, y_perm=b["y_perm"])
+    moe.moe_unpermute(b["y_perm"], p.inv_map, di.w, y=b["y"])
+    moe.moe_unpermute_backward(dy, b["y_perm"], p.inv_map, di.w, dy_perm=b["dy_perm"], d_routing_w=b["d_rw"])
+    moe.moe_grouped_dgrad(b["dy_perm"], p.offsets, di.w_down, "in_out", dx=b["dh"])
+    moe.moe_grouped_wgrad(b["h_buf"], b["dy_perm"], p.offsets, "in_out", dw=b["dw_down"], workspace=b["wws"])
+    moe.moe_swiglu_backward(b["dh"], b["u"], p.offsets, du=b["du"])
+    moe.moe_grouped_dgrad(b["du"], p.offsets, di.w_ug, "out_in", dx=b["dx_perm"])
+    moe.moe_grouped_wgrad(p.x_perm, b["du"], p.offsets, "out_in", dw=b["dw_ug"], workspace=b["wws"])
+    moe.moe_permute_backward(b["dx_perm"], p.inv_map, dx=b["dx"])
+
+
+def test_training_step_graph_replays():
+    """Forward (keeping U) and backward of the expert step captured in one graph; replays match eager runs."""
+    wl = make_random(T=1200, k=4, E=9, d=256, h=192, seed=12, drop_frac=0.1, empty_experts=(2,))
+    say(f"[gpu] graph capture of the training step: T={wl.T} k={wl.k} E={wl.E} d={wl.d} h={wl.h}")
+    dev = torch.device("cuda:0")
+    di = DeviceInputs(wl)
+    b = _train_buffers(wl, dev)
+    dy = torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device=dev)
+    rng = np.random.default_rng(5)
+    dy.copy_(torch.from_numpy(rng.standard_normal((wl.T, wl.d)).astype(np.float32)).to(torch.bfloat16))
+    _train_step(di, b, dy)  # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            _train_step(di, b, dy)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        di.x.copy_(torch.from_numpy(rng.standard_normal(tuple(di.x.shape)).astype(np.float32)).to(torch.bfloat16))
+        dy.copy_(torch.from_numpy(rng.standard_normal((wl.T, wl.d)).astype(np.float32)).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        ref = _train_buffers(wl, dev)
+        _train_step(di, ref, dy)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        M = int(ref["offsets"][-1].item())
+        for key in ("y", "dx", "dw_down", "dw_ug", "d_rw", "u", "du"):
+            a, r = b[key], ref[key]
+            if key in ("u", "du"):
+                a, r = a[:M], r[:M]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               r.view(torch.int16) if r.dtype == torch.bfloat16 else r), f"replay {rep}: {key} differs"
+        say(f"  replay {rep} matches the eager training step")
