@@ -49,7 +49,7 @@ def useful_flops(M: int, d: int, h: int) -> int:
 
 
 def algorithmic_bytes(T, k, M, d, h, nonempty, fused=True):
-    """Bytes each stage must move at minimum (bf16 = 2 B, int32/fp32 = 4 B); see the design doc.
+    """Bytes each stage must move at minimum (bf16 = 2 B, int32/fp32 = 4 B).
 
     fused: the permute writes index maps only and the gate/up GEMM reads each token row of X once at minimum;
     otherwise the permute also copies rows into x_perm, which the GEMM reads back.
