@@ -1,0 +1,44 @@
+"""bench.py's host-side contract, on the CPU: one GPU only, and its FLOP and byte models."""
+
+import os
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    err = capsys.readouterr().err
+    assert "one GPU only" in err
+
+
+def test_world_size_above_one_exits(monkeypatch, capsys):
+    monkeypatch.setenv("WORLD_SIZE", "8")
+    assert bench.main([]) == 2
+    assert "WORLD_SIZE=8" in capsys.readouterr().err
+
+
+def test_useful_flops_follow_the_six_mdh_convention():
+    # the four-expert toy: M = 10 rows, d = 64, h = 128 -> 491,520 useful FLOP
+    assert bench.useful_flops(10, 64, 128) == 491_520
+    # one GPU's share of the Zipf-skewed layer: 65,536 rows, d = 2048, h = 768
+    assert bench.useful_flops(65536, 2048, 768) == 618_475_290_624
+
+
+def test_algorithmic_bytes_of_the_fused_step():
+    T, k, M, d, h, E = 8192, 8, 65536, 2048, 768, 60
+    b = bench.algorithmic_bytes(T, k, M, d, h, E, fused=True)
+    gemm1 = 2 * T * d + E * 2 * (2 * h) * d + 2 * M * h
+    assert b["gemm_up_swiglu"] == gemm1 == 511_705_088
+    unfused = bench.algorithmic_bytes(T, k, M, d, h, E, fused=False)
+    # the unfused path copies rows into x_perm: the permute reads X and writes x_perm, GEMM 1 reads x_perm
+    assert unfused["permute"] - b["permute"] == 2 * T * d + 2 * M * d
+    assert unfused["gemm_up_swiglu"] - b["gemm_up_swiglu"] == 2 * M * d - 2 * T * d
+
+
+@pytest.mark.parametrize("peak,bw,intensity,expect", [(2500.0, 8000.0, 1000.0, 2500.0), (2500.0, 8000.0, 0.1, 800.0)])
+def test_roofline_attainable(peak, bw, intensity, expect):
+    assert bench.roofline_attainable(intensity, bw, peak) == pytest.approx(expect)
