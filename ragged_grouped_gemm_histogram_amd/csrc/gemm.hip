@@ -1103,11 +1103,11 @@ hipError_t launch_kernel(Kern kern, bool* attr_done, const GemmArgs& g, hipStrea
   return hipGetLastError();
 }
 
-// Tile configurations. Large expert blocks (mean rows per expert >= 384) take
-// 256 x 256 tiles on 8 waves (two per SIMD, so one wave's LDS and barrier waits
-// overlap the other's MFMAs) with a 2-stage ring; smaller blocks take 128 x 256
-// tiles on 8 waves with a 3-stage ring, which wastes fewer rows on ragged
-// tails. K not a multiple of 64, or operands too large for 32-bit load
+// Tile configurations. Large expert blocks (mean rows per expert >= 384, and
+// enough 256-row tiles to occupy the device) take 256 x 256 tiles on 8 waves
+// (two per SIMD, so one wave's LDS and barrier waits overlap the other's MFMAs)
+// with a 2-stage ring; smaller blocks take 128 x 256 tiles on 8 waves with a
+// 3-stage ring, which wastes fewer rows on ragged tails. K not a multiple of 64, or operands too large for 32-bit load
 // offsets, take the register-staged loop.
 template <bool GATED>
 using BigTile = Tile<256, 256, 2, 4, 2, GATED>;
@@ -1128,7 +1128,12 @@ inline bool offsets_fit_32(const GemmArgs& g) {
 template <bool GATED, bool B_NMAJOR, bool SAVE_U = false>
 hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
   if (g.K % BK == 0 && offsets_fit_32(g)) {
-    if (g.cap_rows >= (int64_t)384 * g.E) {
+    // 256-row tiles need large expert blocks, and enough of them to occupy every CU: at most
+    // cap_rows/256 + E row tiles exist whatever the offsets; when even that many cannot fill the
+    // device, 128-row tiles (twice the tiles, a deeper ring) finish sooner.
+    const int64_t tile_n = GATED ? BigTile<GATED>::OUTW : BigTile<GATED>::BN;
+    const int64_t big_tiles = (g.cap_rows / BigTile<GATED>::BM + g.E) * ((g.N + tile_n - 1) / tile_n);
+    if (g.cap_rows >= (int64_t)384 * g.E && big_tiles >= device_cu_count(current_device())) {
       static bool done[64] = {};
       return launch_kernel<BigTile<GATED>>(grouped_gemm_pipe_kernel<BigTile<GATED>, B_NMAJOR, SAVE_U>, done, g, stream);
     }

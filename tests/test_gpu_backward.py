@@ -36,7 +36,7 @@ def _case(seed, counts, d_in, d_out, extra_rows=8, x_sigma=1.0, w_sigma=0.05):
 CASES = [
     # counts, d_in, d_out
     ([0, 37, 300, 1, 129, 0, 513], 320, 576),      # ragged, empty experts, 128-row forward tiles
-    ([700, 900, 420], 256, 512),                    # 256-row forward tiles, tails in every expert's last stage
+    ([700, 900, 420], 6656, 256),                   # 256-row forward tiles (Dgrad), tails in every expert's last stage
     ([5, 0, 260, 77], 328, 200),                    # widths not multiples of 64
     ([1], 64, 64),                                  # one row
     ([64, 128, 65, 63], 264, 136),                  # contraction lengths at and around one stage

@@ -82,9 +82,13 @@ def _fuzz_cases():
         dict(T=64, k=4, E=1, d=8, h=8, seed=4, drop_frac=0.0),
         dict(T=40, k=2, E=1024, d=64, h=64, seed=5, drop_frac=0.1),
         dict(T=33, k=2, E=6, d=64, h=64, seed=6, drop_frac=1.0),  # every slot dropped: M = 0
-        # K % 64 == 0 with N and M tails: large blocks (>= 384 rows per expert) take the 256 x 256
-        # tile, smaller ones the 128 x 256 tile
+        # K % 64 == 0 with N and M tails: large blocks (>= 384 rows per expert) whose 256-row tiles
+        # can fill the device take the 256 x 256 tile, others the 128 x 256 tile
         dict(T=900, k=2, E=3, d=320, h=192, seed=7, drop_frac=0.05),
+        # (weights scaled down, as in the named workloads, so that the long contractions keep
+        # activations of order one and the contract's absolute bound stays meaningful)
+        dict(T=1000, k=2, E=3, d=128, h=4480, seed=12, drop_frac=0.05, w_sigma=0.04),  # 256-row tiles, gate/up side
+        dict(T=1000, k=2, E=3, d=8768, h=64, seed=13, drop_frac=0.05, empty_experts=(1,), w_sigma=0.015),  # down side
         dict(T=200, k=3, E=4, d=320, h=192, seed=8, drop_frac=0.05, empty_experts=(2,)),
         dict(T=1100, k=1, E=2, d=576, h=448, seed=9, drop_frac=0.0),
         # many tiles per workgroup with one or two K stages per tile: the load stream runs
@@ -105,9 +109,12 @@ def test_random_cases(case):
     y, p, h_buf, y_perm = run_path(wl)
     ref = oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
     check_all(wl, ref, y, p, h_buf, y_perm)
+    # the down projection alone, from the GPU's own h_buf: its error without GEMM 1's roundings
+    M = ref.M
+    chained = oracle.grouped_projection(bits(h_buf)[:M], ref.offsets, wl.w_down)
+    say("  y_perm from the GPU's h_buf " + str(compare_bf16(bits(y_perm)[:M], chained, "y_perm (chained)")))
     # the fused-gather path runs the same arithmetic on the same rows: identical bits
     y2, p2, h2, yp2 = run_path(wl, fused=True)
-    M = ref.M
     assert torch.equal(y2, y) and torch.equal(h2[:M], h_buf[:M]) and torch.equal(yp2[:M], y_perm[:M])
 
 

@@ -53,7 +53,7 @@ def _check_sampled(a, w, y, offsets, per_expert=2, seed=0, what="y"):
 
 @pytest.mark.parametrize("counts,K,N", [
     ([0, 37, 300, 1, 129, 0, 513], 320, 576),   # ragged, empty experts, 128-row tiles
-    ([700, 900, 420], 256, 512),                 # mean >= 384 rows: 256-row tiles
+    ([700, 900, 420, 0, 1100], 192, 8712),       # large blocks, enough tiles to fill the device: 256-row tiles
     ([5, 0, 260, 77], 328, 200),                 # K and N not multiples of 64: register-staged loop
     ([1], 64, 64),                               # one row
 ], ids=["ragged", "big-tiles", "k-tail", "one-row"])
@@ -76,7 +76,7 @@ def test_projection_whole(counts, K, N):
 @pytest.mark.parametrize("counts,K,N", [
     ([50000] * 4, 64, 512),               # 256-row tiles, one K stage each, ~6 tiles per workgroup
     ([100] * 300 + [0] * 20 + [37] * 280, 64, 1024),  # 128-row tiles (3-slot ring), one K stage each
-    ([3000] * 7 + [5], 128, 256),         # two K stages per tile
+    ([3000] * 2 + [5], 128, 8192),        # 256-row tiles, two K stages each
 ], ids=["big-k64", "small-k64", "big-k128"])
 def test_projection_stream_across_tiles(counts, K, N):
     """Several tiles per workgroup with fewer K stages than ring slots: the loads of the next
