@@ -89,11 +89,13 @@ def test_wgrad_empty_capacity_writes_zeros():
 
 
 @pytest.mark.timeout(900)
-def test_backward_at_expert_shapes():
-    """The backward GEMMs of the zipf64 expert step at full size (64 experts, d = 2048, h = 768,
-    65,536 rows): Dgrad and Wgrad of the down projection ([E, h, d]) and of the gate/up projection
-    ([E, 2h, d]), checked on sampled rows of every output against the oracle."""
-    wl = make_workload("zipf64")
+@pytest.mark.parametrize("name", ["zipf64", "qwen3_30b", "square"])
+def test_backward_at_expert_shapes(name):
+    """The backward GEMMs of a named expert step at full size (zipf64: 64 experts, d = 2048, h = 768,
+    65,536 rows, experts above the Wgrad split; Qwen3-shaped: 128 experts of about 256 rows;
+    square: d = h = 2880): Dgrad and Wgrad of the down projection ([E, h, d]) and of the gate/up
+    projection ([E, 2h, d]), checked on sampled rows of every output against the oracle."""
+    wl = make_workload(name)
     di = DeviceInputs(wl)
     y, p, h_buf, y_perm = moe.moe_expert_forward(di.x, di.ids, di.w, di.w_ug, di.w_down, fused_gather=False)
     M = int(p.offsets[-1].item())
@@ -103,10 +105,10 @@ def test_backward_at_expert_shapes():
         torch.bfloat16).to("cuda:0")
     g_u = torch.from_numpy(to_bf16_bits(rng.standard_normal((wl.S, 2 * wl.h), dtype=np.float32)).view(np.int16)).view(
         torch.bfloat16).to("cuda:0")
-    say("[gpu] zipf64 down projection: Dgrad (h <- d) and Wgrad [E, h, d]")
+    say(f"[gpu] {name} down projection: Dgrad (h <- d) and Wgrad [E, h, d]")
     dh = moe.moe_grouped_dgrad(g_y, p.offsets, di.w_down, "in_out")
     dwd = moe.moe_grouped_wgrad(h_buf, g_y, p.offsets, "in_out")
-    say("[gpu] zipf64 gate/up projection: Dgrad (d <- 2h) and Wgrad [E, 2h, d]")
+    say(f"[gpu] {name} gate/up projection: Dgrad (d <- 2h) and Wgrad [E, 2h, d]")
     dx = moe.moe_grouped_dgrad(g_u, p.offsets, di.w_ug, "out_in")
     dwu = moe.moe_grouped_wgrad(p.x_perm, g_u, p.offsets, "out_in")
     torch.cuda.synchronize()
