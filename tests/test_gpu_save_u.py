@@ -72,3 +72,22 @@ def test_backward_with_saved_u_matches_recompute():
             ga, gb = ga[:M], gb[:M]
         assert torch.equal(ga.view(torch.int16), gb.view(torch.int16)), f"{key} differs with the saved U"
     assert torch.equal(a["d_routing_w"], b["d_routing_w"])
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["zipf64", "qwen3_30b", "square"])
+def test_save_u_at_full_size(name):
+    """The named workloads' gate/up launch with U kept: h_buf equal to the plain launch's and U equal to the
+    grouped projection's, bit for bit (each element runs the same MFMA sequence in the three launches)."""
+    from gpu_util import workload
+    wl = workload(name)
+    say(f"[gpu] save-U at full size: {name}")
+    di = DeviceInputs(wl)
+    p = moe.moe_permute(di.x, di.ids, wl.E, gather=True)
+    h_plain = moe.moe_gemm_up_swiglu(p.x_perm, p.offsets, di.w_ug)
+    h_u, u = moe.moe_gemm_up_swiglu_u(p.x_perm, p.offsets, di.w_ug)
+    u_proj = moe.moe_grouped_projection(p.x_perm, p.offsets, di.w_ug, "out_in")
+    torch.cuda.synchronize()
+    M = int(p.offsets[-1].item())
+    assert torch.equal(h_u[:M].view(torch.int16), h_plain[:M].view(torch.int16)), "h_buf differs from the plain launch"
+    assert torch.equal(u[:M].view(torch.int16), u_proj[:M].view(torch.int16)), "U differs from the grouped projection"
