@@ -88,6 +88,10 @@ def _check(status: int, call: str) -> None:
 
 
 def _stream(t: torch.Tensor) -> int:
+    # The library launches on the current HIP device; a stream of another device would fail the launch.
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors are on {t.device} but the current device is cuda:{torch.cuda.current_device()}; "
+                         "call inside torch.cuda.device(...)")
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -380,15 +384,16 @@ def moe_grouped_wgrad(x: torch.Tensor, dy: torch.Tensor, offsets: torch.Tensor, 
     _want(x, "x", torch.bfloat16, (cap, d_in), dev)
     _want(dy, "dy", torch.bfloat16, (cap, d_out), dev)
     _want(offsets, "offsets", torch.int32, (E + 1,), dev)
-    shape = (E, d_in, d_out) if layout == "in_out" else (E, d_out, d_in)
     if layout not in W_LAYOUTS:
         raise ValueError(f"layout must be one of {sorted(W_LAYOUTS)}, got {layout!r}")
+    shape = (E, d_in, d_out) if layout == "in_out" else (E, d_out, d_in)
     dw = _out(dw, "dw", torch.bfloat16, shape, dev)
     need = wgrad_workspace_bytes(cap, d_in, d_out, E)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace must hold {need} bytes on {dev}")
+    if (workspace.device != dev or not workspace.is_contiguous()
+            or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on {dev}")
     _check(load_library().moe_grouped_wgrad(_ptr(x), _ptr(dy), _ptr(offsets), W_LAYOUTS[layout], cap, d_in, d_out, E,
                                             _ptr(dw), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream(x)), "moe_grouped_wgrad")
