@@ -95,6 +95,8 @@ def _fuzz_cases():
         # across tile boundaries (256-row tiles on the gate/up side, 128-row on the down side)
         dict(T=20000, k=2, E=8, d=64, h=256, seed=10, drop_frac=0.02),
         dict(T=6000, k=4, E=96, d=128, h=64, seed=11, drop_frac=0.1, empty_experts=(5, 50)),
+        # many slots per token (duplicates within a token included): the unpermute sums 16 rows
+        dict(T=300, k=16, E=40, d=136, h=96, seed=14, drop_frac=0.1, empty_experts=(7,)),
     ]
     return cases
 
