@@ -15,8 +15,10 @@ step captured once in a HIP graph, which is the headline unless --eager.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config zipf64]
 Prints one JSON line. Extra measurements ride along in the same line:
 per-stage times, the padded-BMM and per-expert-loop variants (vendor BLAS
-through torch, same inputs), the roofline of the dominant kernel and the CPU
-oracle timed on a bounded sample of the same workload.
+through torch, same inputs), the roofline of the dominant kernel, the CPU
+oracle timed on a bounded sample of the same workload, and the GPU clock and
+socket power read during a steady back-to-back loop after the timed region
+(the OLMo report ties its largest-shape results to the clock under power limits).
 """
 
 from __future__ import annotations
@@ -96,6 +98,104 @@ def cpu_baseline(wl, tokens: int, min_seconds: float = 10.0):
             "numpy": np.__version__}
 
 
+def summarize_telemetry(samples, t0: float, t1: float, settle: float = 0.25):
+    """Clock and power over the steady part of a back-to-back loop.
+
+    samples: (time, per-XCD gfx clocks in MHz, socket power in W, gfx activity in %) tuples; entries that the
+    driver reports as unavailable (anything not a number) are skipped. The first `settle` fraction of the loop
+    (clock ramp) is left out.
+    """
+    lo = t0 + settle * (t1 - t0)
+    steady = [s for s in samples if lo <= s[0] <= t1]
+
+    def nums(vals):
+        return [float(v) for v in vals if isinstance(v, (int, float)) and not isinstance(v, bool) and v > 0]
+
+    clk = [sum(c) / len(c) for c in (nums(s[1] or []) for s in steady) if c]
+    pwr = nums([s[2] for s in steady])
+    act = nums([s[3] for s in steady])
+
+    def stats(v):
+        if not v:
+            return None
+        v = sorted(v)
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]}
+
+    return {"samples": len(steady), "gfx_clock_mhz": stats(clk), "socket_power_w": stats(pwr),
+            "gfx_activity_pct": stats(act)}
+
+
+def steady_telemetry(torch, run_step, ms_per_step: float, seconds: float = 1.5, interval_s: float = 0.02):
+    """GPU clock and socket power read through amdsmi (read-only queries) while the step runs back to back.
+
+    The loop is separate from the timed region. Returns {"error": ...} when the library or the device is not
+    reachable; the benchmark line is printed either way.
+    """
+    import threading
+
+    try:
+        import amdsmi
+    except Exception as exc:  # the python bindings are not installed
+        return {"error": f"amdsmi not importable ({type(exc).__name__})"}
+    try:
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+    except Exception as exc:
+        return {"error": f"amdsmi_init failed ({type(exc).__name__}: {exc})"}
+    try:
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+        handles = amdsmi.amdsmi_get_processor_handles()
+        handle = None
+        for hd in handles:
+            dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(hd).split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                handle = hd
+                break
+        if handle is None:
+            return {"error": f"no amdsmi device at PCI {want[0]:04x}:{want[1]:02x}:{want[2]:02x} "
+                             f"({len(handles)} visible)"}
+        n = max(1, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
+        samples, done = [], threading.Event()
+
+        def sampler():
+            while not done.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                    clks = m.get("current_gfxclks")
+                    samples.append((time.perf_counter(), clks if isinstance(clks, list) else [],
+                                    m.get("current_socket_power"), m.get("average_gfx_activity")))
+                except Exception:  # one failed read drops one sample
+                    pass
+                time.sleep(interval_s)
+
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            run_step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        done.set()
+        th.join()
+        out = summarize_telemetry(samples, t0, t1)
+        out.update({"steps": n, "seconds": t1 - t0, "source": "amdsmi gpu_metrics (current_gfxclks averaged over "
+                    "XCDs, current_socket_power), steady part of a back-to-back loop"})
+        try:
+            cap = amdsmi.amdsmi_get_power_info(handle).get("power_limit")  # microwatts
+            out["power_limit_w"] = cap / 1e6 if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception:
+            out["power_limit_w"] = None
+        return out
+    except Exception as exc:
+        return {"error": f"{type(exc).__name__}: {exc}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +209,8 @@ def main(argv=None):
                     help="copy rows into x_perm in moe_permute instead of gathering them inside the gate/up GEMM")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the clock and power readings taken during a steady loop after the timed region")
     ap.add_argument("--eager", action="store_true",
                     help="report eager launches as the headline instead of replays of the step captured in a HIP graph")
     ap.add_argument("--sweep", choices=SWEEPS,
@@ -193,6 +295,7 @@ def main(argv=None):
 
     eager_ms = elapsed * 1e3 / args.steps
     graph_ms, graph_note = None, None
+    replay = None
     if not args.eager:
         # The same step captured once in a HIP graph (the library allocates, synchronises and copies
         # nothing, so its calls capture as they are), then exactly K replays timed like the eager
@@ -213,6 +316,7 @@ def main(argv=None):
                 g.replay()
             torch.cuda.synchronize()
             graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+            replay = g.replay
         except Exception as exc:  # capture unavailable: the eager time stays the headline
             graph_note = f"graph capture failed ({type(exc).__name__}: {exc}); eager launches reported"
             torch.cuda.synchronize()
@@ -220,6 +324,8 @@ def main(argv=None):
     M = int(offsets[-1].item())
     nonempty = int((counts > 0).sum().item())
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    # Clock and power during about 1.5 s of the headline step back to back (after the timed region).
+    telemetry = None if args.no_telemetry else steady_telemetry(torch, replay or step, ms_per_step)
     flops = useful_flops(M, d, h)
     value = flops / (ms_per_step * 1e-3) / 1e12
     names = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
@@ -298,6 +404,7 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": cpu,
         "variants": variants,
+        "telemetry": telemetry,
     }
     print(json.dumps(out))
     return 0

@@ -42,3 +42,18 @@ def test_algorithmic_bytes_of_the_fused_step():
 @pytest.mark.parametrize("peak,bw,intensity,expect", [(2500.0, 8000.0, 1000.0, 2500.0), (2500.0, 8000.0, 0.1, 800.0)])
 def test_roofline_attainable(peak, bw, intensity, expect):
     assert bench.roofline_attainable(intensity, bw, peak) == pytest.approx(expect)
+
+
+def test_telemetry_summary_keeps_the_steady_part_and_skips_unavailable_readings():
+    # (time, per-XCD clocks, socket power, activity); the driver marks missing readings "N/A"
+    samples = [(0.1, [1000] * 8, 500, 50),            # inside the settle window: dropped
+               (0.5, [2000, 2100, "N/A", 1900], 1300, 99),
+               (0.7, [1800] * 8, "N/A", 100),
+               (0.9, ["N/A"] * 8, 1350, "N/A"),
+               (1.5, [2400] * 8, 1400, 100)]           # after the loop ended: dropped
+    out = bench.summarize_telemetry(samples, t0=0.0, t1=1.0)
+    assert out["samples"] == 3
+    assert out["gfx_clock_mhz"] == {"median": 2000.0, "min": 1800.0, "max": 2000.0}
+    assert out["socket_power_w"] == {"median": 1350.0, "min": 1300.0, "max": 1350.0}
+    assert out["gfx_activity_pct"]["max"] == 100.0
+    assert bench.summarize_telemetry([], 0.0, 1.0)["gfx_clock_mhz"] is None
