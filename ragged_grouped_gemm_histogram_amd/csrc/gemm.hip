@@ -591,7 +591,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
     // once, both can stall on load issue while neither issues MFMAs. Their loads still have
     // three of the four slices to land (issuing them two slices late instead was 10% slower).
     // Bit-identical results; the 256-row gate/up GEMM 2% faster on the zipf64 and square workloads.
-    const bool late_issue = kPrefetch && NST == 2 && C::NWAVES == 8 && wave >= 4;
+    // The launch that also keeps U has no registers to spare for it (the compiler spills).
+    const bool late_issue = kPrefetch && !SAVE_U && NST == 2 && C::NWAVES == 8 && wave >= 4;
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
       if (s < nk) issue(s);
