@@ -74,5 +74,43 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB_PATH
 
 
+# Host-sanitizer build (CPU tests only): host code with AddressSanitizer and
+# UndefinedBehaviorSanitizer. Each sanitizer flag is scoped to the host compilation
+# with -Xarch_host; the device code is built as usual and never run from this library.
+SAN_DIR = os.path.join(BUILD_DIR, "host_sanitized")
+SAN_LIB_PATH = os.path.join(SAN_DIR, "libmoe_grouped_host_sanitized.so")
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def clangxx() -> str:
+    path = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    return os.path.realpath(path) if os.path.exists(path) else "/opt/rocm/llvm/bin/clang++"
+
+
+def sanitizer_runtime() -> str:
+    """The shared AddressSanitizer runtime the sanitized library needs preloaded (LD_PRELOAD)."""
+    res = subprocess.run([clangxx(), "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    return res.stdout.strip()
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Host-only objects with ASan and UBSan, linked with the shared sanitizer runtime; returns the path."""
+    cc = hipcc()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    flags = [f for f in HIP_FLAGS if f != "-O3"] + ["-O1", *SAN_HOST_FLAGS]
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(SAN_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    rocm_lib = os.path.realpath(os.path.join(os.path.dirname(os.path.realpath(cc)), "..", "lib"))
+    _run([clangxx(), "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", "-o", SAN_LIB_PATH, *objs,
+          f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{rocm_lib}"], verbose)
+    return SAN_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -294,8 +294,14 @@ moe_status moe_unpermute_backward(const uint16_t* dy, const uint16_t* y_perm, co
   return launched(launch_unpermute_backward(dy, y_perm, inv_map, routing_w, T, k, d, dy_perm, d_routing_w, stream));
 }
 
+static_assert(sizeof(moe_status) == sizeof(int), "moe_status travels as a C int");
+
 const char* moe_status_string(moe_status s) {
-  switch (s) {
+  // A C caller may pass any int. In C++ an enum without a fixed underlying type only holds
+  // the values of its enumerators' bit width, so the code is read as raw int bits.
+  int code;
+  std::memcpy(&code, &s, sizeof(code));
+  switch (code) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_NULL_POINTER: return "MOE_ERR_NULL_POINTER: a pointer is NULL while its tensor is non-empty";
     case MOE_ERR_BAD_SHAPE: return "MOE_ERR_BAD_SHAPE: a size is out of range (T, k, E, d, h or T*k)";

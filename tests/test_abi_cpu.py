@@ -6,6 +6,7 @@ GPU (it must report MOE_ERR_UNSUPPORTED_DEVICE, not crash).
 """
 
 import ctypes
+import os
 
 import pytest
 import torch
@@ -13,6 +14,12 @@ import torch
 import ragged_grouped_gemm_histogram_amd as moe
 
 OK, NULLP, SHAPE, ALIGN, WS, DEV, LAUNCH = range(7)
+
+# The host-sanitizer test re-runs this file against a build whose host code carries
+# AddressSanitizer and UndefinedBehaviorSanitizer checks.
+if os.environ.get("MOE_TEST_LIB"):
+    moe.LIB_PATH = os.environ["MOE_TEST_LIB"]
+    moe._LIB = None
 
 
 @pytest.fixture(scope="module")
