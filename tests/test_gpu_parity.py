@@ -97,6 +97,10 @@ def _fuzz_cases():
         dict(T=6000, k=4, E=96, d=128, h=64, seed=11, drop_frac=0.1, empty_experts=(5, 50)),
         # many slots per token (duplicates within a token included): the unpermute sums 16 rows
         dict(T=300, k=16, E=40, d=136, h=96, seed=14, drop_frac=0.1, empty_experts=(7,)),
+        # 256-row gate/up tiles over three and four K stages: the second wave of each SIMD issues its
+        # half of a stage's loads one slice after the first (and the first two stages start together)
+        dict(T=4096, k=2, E=4, d=192, h=1024, seed=15, drop_frac=0.03),
+        dict(T=4096, k=2, E=4, d=256, h=1024, seed=16, drop_frac=0.0, empty_experts=(2,)),
     ]
     return cases
 
