@@ -121,11 +121,30 @@ def summarize_telemetry(samples, t0: float, t1: float, settle: float = 0.25):
         v = sorted(v)
         return {"median": v[len(v) // 2], "min": v[0], "max": v[-1]}
 
-    return {"samples": len(steady), "gfx_clock_mhz": stats(clk), "socket_power_w": stats(pwr),
-            "gfx_activity_pct": stats(act)}
+    distinct = len({(tuple(nums(s[1] or [])), s[2], s[3]) for s in steady})
+    return {"samples": len(steady), "distinct_readings": distinct, "gfx_clock_mhz": stats(clk),
+            "socket_power_w": stats(pwr), "gfx_activity_pct": stats(act)}
 
 
-def steady_telemetry(torch, run_step, ms_per_step: float, seconds: float = 1.5, interval_s: float = 0.02):
+def energy_average_power(e0, e1, host_seconds: float):
+    """Average power from two energy-counter readings (accumulator, microjoules per count, timestamp).
+
+    The timestamp's unit is not fixed across library versions: it is taken as the power of ten that makes the
+    counter's interval closest to the host's. Returns (watts, seconds) or (None, None).
+    """
+    try:
+        de = (e1["energy_accumulator"] - e0["energy_accumulator"]) * float(e0["counter_resolution"]) * 1e-6
+        dts = e1["timestamp"] - e0["timestamp"]
+    except (KeyError, TypeError):
+        return None, None
+    if de <= 0 or dts <= 0 or host_seconds <= 0:
+        return None, None
+    unit = min((1e9, 1e8, 1e6, 1e3), key=lambda u: abs(math.log(dts / u / host_seconds)))
+    secs = dts / unit
+    return de / secs, secs
+
+
+def steady_telemetry(torch, run_step, ms_per_step: float, seconds: float = 3.0, interval_s: float = 0.02):
     """GPU clock and socket power read through amdsmi (read-only queries) while the step runs back to back.
 
     The loop is separate from the timed region. Returns {"error": ...} when the library or the device is not
@@ -168,19 +187,34 @@ def steady_telemetry(torch, run_step, ms_per_step: float, seconds: float = 1.5, 
                     pass
                 time.sleep(interval_s)
 
+        def energy():
+            try:
+                return amdsmi.amdsmi_get_energy_count(handle)
+            except Exception:  # no energy counter on this device or library
+                return None
+
         torch.cuda.synchronize()
         th = threading.Thread(target=sampler, daemon=True)
         th.start()
         t0 = time.perf_counter()
-        for _ in range(n):
+        for _ in range(n // 4):  # settle: the clock and the counters' windows fill with the loop
             run_step()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
+        e0, te0 = energy(), time.perf_counter()
+        for _ in range(n - n // 4):
+            run_step()
+        torch.cuda.synchronize()
+        e1, t1 = energy(), time.perf_counter()
         done.set()
         th.join()
         out = summarize_telemetry(samples, t0, t1)
+        watts, secs = energy_average_power(e0, e1, t1 - te0) if e0 and e1 else (None, None)
+        out["energy_average_power_w"] = watts
+        out["energy_interval_s"] = secs
         out.update({"steps": n, "seconds": t1 - t0, "source": "amdsmi gpu_metrics (current_gfxclks averaged over "
-                    "XCDs, current_socket_power), steady part of a back-to-back loop"})
+                    "XCDs, current_socket_power) sampled every 20 ms over the last three quarters of a back-to-back "
+                    "loop (the driver refreshes the table less often: distinct_readings counts the fresh ones), and "
+                    "the energy counter's average over the same three quarters"})
         try:
             cap = amdsmi.amdsmi_get_power_info(handle).get("power_limit")  # microwatts
             out["power_limit_w"] = cap / 1e6 if isinstance(cap, (int, float)) and cap > 0 else None

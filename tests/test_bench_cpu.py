@@ -57,3 +57,15 @@ def test_telemetry_summary_keeps_the_steady_part_and_skips_unavailable_readings(
     assert out["socket_power_w"] == {"median": 1350.0, "min": 1300.0, "max": 1350.0}
     assert out["gfx_activity_pct"]["max"] == 100.0
     assert bench.summarize_telemetry([], 0.0, 1.0)["gfx_clock_mhz"] is None
+
+
+def test_energy_average_power_picks_the_timestamp_unit():
+    # 2 s at 1,350 W in 15.3 uJ counts, timestamps in nanoseconds and in 10 ns ticks
+    counts = 1350.0 * 2.0 / 15.3e-6
+    e0 = {"energy_accumulator": 1000, "counter_resolution": 15.3, "timestamp": 5_000_000_000}
+    for unit in (1e9, 1e8):
+        e1 = {"energy_accumulator": 1000 + counts, "counter_resolution": 15.3,
+              "timestamp": 5_000_000_000 + int(2.0 * unit)}
+        watts, secs = bench.energy_average_power(e0, e1, host_seconds=2.05)
+        assert secs == pytest.approx(2.0) and watts == pytest.approx(1350.0, rel=1e-6)
+    assert bench.energy_average_power(e0, dict(e0), 1.0) == (None, None)  # no energy counted
