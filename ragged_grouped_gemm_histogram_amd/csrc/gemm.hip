@@ -42,6 +42,8 @@
 //    fill for the K remainder, double-buffered, 128 x 256 tiles on 4 waves;
 //    N-contiguous blocks of 8(k) x 8(n) are transposed in registers.
 
+#include <atomic>
+
 #include "common.h"
 
 namespace moe {
@@ -1100,13 +1102,15 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradArgs g) {
 }
 
 template <class C, typename Kern>
-hipError_t launch_kernel(Kern kern, bool* attr_done, const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_kernel(Kern kern, std::atomic<bool>* attr_done, const GemmArgs& g, hipStream_t stream) {
   const int dev = current_device();
-  if (dev >= 0 && dev < 64 && !attr_done[dev]) {
+  // Threads launching on one device may race to set the attribute the first time: setting it twice is harmless,
+  // and the flag is atomic so that the race itself is well-defined.
+  if (dev >= 0 && dev < 64 && !attr_done[dev].load(std::memory_order_acquire)) {
     hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                         C::LDS_BYTES);
     if (st != hipSuccess) return st;
-    attr_done[dev] = true;
+    attr_done[dev].store(true, std::memory_order_release);
   }
   const int grid = device_cu_count(dev);  // one workgroup per CU: the LDS ring fills it
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, stream, g);
@@ -1144,14 +1148,14 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
     const int64_t tile_n = GATED ? BigTile<GATED>::OUTW : BigTile<GATED>::BN;
     const int64_t big_tiles = (g.cap_rows / BigTile<GATED>::BM + g.E) * ((g.N + tile_n - 1) / tile_n);
     if (g.cap_rows >= (int64_t)384 * g.E && big_tiles >= device_cu_count(current_device())) {
-      static bool done[64] = {};
+      static std::atomic<bool> done[64] = {};
       return launch_kernel<BigTile<GATED>>(grouped_gemm_pipe_kernel<BigTile<GATED>, B_NMAJOR, SAVE_U>, done, g, stream);
     }
-    static bool done[64] = {};
+    static std::atomic<bool> done[64] = {};
     return launch_kernel<SmallTile<GATED>>(grouped_gemm_pipe_kernel<SmallTile<GATED>, B_NMAJOR, SAVE_U>, done, g,
                                            stream);
   }
-  static bool done[64] = {};
+  static std::atomic<bool> done[64] = {};
   return launch_kernel<RegsTile<GATED>>(grouped_gemm_regs_kernel<RegsTile<GATED>, B_NMAJOR, SAVE_U>, done, g, stream);
 }
 
@@ -1200,7 +1204,7 @@ hipError_t launch_grouped_wgrad(const uint16_t* x, const uint16_t* dy, const int
   const int64_t slots = wgrad_partial_slots(cap_rows);
   const WgradArgs g = !w_out_in ? WgradArgs{x, d_in, dy, d_out, d_in, d_out, offsets, E, cap_rows, dw, partial, slots}
                                 : WgradArgs{dy, d_out, x, d_in, d_out, d_in, offsets, E, cap_rows, dw, partial, slots};
-  static bool done[64] = {};
+  static std::atomic<bool> done[64] = {};
   const int dev = current_device();
   if (dev >= 0 && dev < 64 && !done[dev]) {
     hipError_t st = hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_wgrad_kernel<WgradTile>),
