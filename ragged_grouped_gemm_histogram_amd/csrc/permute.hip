@@ -7,7 +7,8 @@
 // per-expert blocks, and a sentinel-padded inverse map records where each slot
 // went.
 //
-// Four launches, none of which needs a count on the host:
+// Four launches (one workgroup for the first three when the dispatch is small, see
+// permute_small_kernel), none of which needs a count on the host:
 //   1. hist     one block per chunk of 256 slots: LDS histogram -> table[e][chunk]
 //   2. colscan  one block per expert: exclusive scan of that expert's row of
 //               the table over chunks (in place) and its total -> counts[e]
@@ -161,6 +162,114 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
+// Small dispatches (at most kSmallChunks chunks and kSmallTable table entries): the
+// three steps above in one workgroup of 16 waves, the per-chunk table in LDS and
+// workgroup barriers in place of kernel boundaries (for a few thousand slots each
+// launch costs more than its work). Same table, same order, same results.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallChunks = 64;
+constexpr int kSmallTable = 8192;  // E * nchunks entries, 32 KB of LDS
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int32_t* __restrict__ ids, int64_t S,
+                                                                      int E, int id_bits, int nchunks,
+                                                                      int32_t* __restrict__ counts,
+                                                                      int32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ perm,
+                                                                      int32_t* __restrict__ inv) {
+  __shared__ int table[kSmallTable];  // [e][chunk]: counts, then starting positions
+  __shared__ int off_s[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int entries = E * nchunks;
+  for (int i = tid; i < entries; i += kSmallThreads) table[i] = 0;
+  __syncthreads();
+  // 1. histogram per chunk (LDS integer atomics: order-free)
+  for (int64_t s = tid; s < S; s += kSmallThreads) {
+    const int e = ids[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&table[e * nchunks + (int)(s / kPermuteChunk)], 1);
+  }
+  __syncthreads();
+  // 2. per expert: exclusive scan over chunks, total -> counts
+  for (int e = tid; e < E; e += kSmallThreads) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = table[e * nchunks + c];
+      table[e * nchunks + c] = run;
+      run += v;
+    }
+    counts[e] = run;
+    off_s[e] = run;  // the scan below turns the totals into offsets
+  }
+  __syncthreads();
+  // offsets = exclusive scan of the totals, by the first wave (a run of 16 experts per lane)
+  if (wave == 0) {
+    constexpr int kPer = (MOE_MAX_EXPERTS + 63) / 64;
+    int run[kPer];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane * kPer + i;
+      run[i] = (e < E) ? off_s[e] : 0;
+      local += run[i];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += up;
+    }
+    int acc = incl - local;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane * kPer + i;
+      if (e < E) off_s[e] = acc;
+      acc += run[i];
+    }
+    if (lane == 63) off_s[E] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += kSmallThreads) offsets[e] = off_s[e];
+  // 3. starting position of every (expert, chunk) run
+  for (int i = tid; i < entries; i += kSmallThreads) table[i] += off_s[i / nchunks];
+  __syncthreads();
+  // 4. wave w walks chunks w, w + 16, ... in steps of 64 slots, as scatter_kernel does; the
+  // loop bounds are the same for every wave so every wave meets every barrier.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < nchunks; c0 += kSmallWaves) {
+    const int c = c0 + wave;
+    for (int step = 0; step < kPermuteChunk / 64; ++step) {
+      const int64_t s = (int64_t)c * kPermuteChunk + step * 64 + lane;
+      const bool in = c < nchunks && s < S;
+      const int e = in ? ids[s] : -1;
+      const bool keep = in && ((unsigned)e < (unsigned)E);
+      uint64_t same = __ballot(keep);
+      for (int b = 0; b < id_bits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+      }
+      const int rank = __popcll(same & lt_mask);
+      const int leader = keep ? (__ffsll((long long)same) - 1) : lane;
+      int base = 0;
+      if (keep && lane == leader) {
+        base = table[e * nchunks + c];
+        table[e * nchunks + c] = base + __popcll(same);
+      }
+      base = __shfl(base, leader, 64);
+      if (in) {
+        if (keep) {
+          const int pos = base + rank;
+          if ((int64_t)pos < S) perm[pos] = (int32_t)s;
+          inv[s] = pos;
+        } else {
+          inv[s] = -1;
+        }
+      }
+      __syncthreads();  // this step's cursor updates are visible to the next
+    }
+  }
+}
+
 // x_perm[p] = x[perm[p] / k] for p < M = offsets[E]; 16-byte chunks.
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(const uint16_t* __restrict__ x,
                                                                 const int32_t* __restrict__ perm,
@@ -206,13 +315,16 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int3
                           int32_t* table, hipStream_t stream) {
   const int64_t S = T * k;
   const int64_t nchunks = permute_chunks(S);
-  if (nchunks > 0) {
+  if (nchunks <= kSmallChunks && (int64_t)E * nchunks <= kSmallTable) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, ids, S, E, bits_for(E),
+                       (int)nchunks, counts, offsets, perm, inv);
+  } else {
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nchunks), dim3(kHistThreads), 0, stream, ids, S, E, table,
                        nchunks);
+    hipLaunchKernelGGL(colscan_kernel, dim3(E), dim3(kScanThreads), 0, stream, table, nchunks, counts);
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nchunks), dim3(64), 0, stream, ids, S, E, bits_for(E), counts,
+                       table, nchunks, offsets, perm, inv);
   }
-  hipLaunchKernelGGL(colscan_kernel, dim3(E), dim3(kScanThreads), 0, stream, table, nchunks, counts);
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(nchunks > 0 ? nchunks : 1)), dim3(64), 0, stream, ids, S, E,
-                     bits_for(E), counts, table, nchunks, offsets, perm, inv);
   if (S > 0 && x_perm != nullptr) {  // no x_perm: the caller gathers inside the GEMM
     const int dev = current_device();
     const int64_t cpr = d / 8;
