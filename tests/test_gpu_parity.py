@@ -101,6 +101,11 @@ def _fuzz_cases():
         # half of a stage's loads one slice after the first (and the first two stages start together)
         dict(T=4096, k=2, E=4, d=192, h=1024, seed=15, drop_frac=0.03),
         dict(T=4096, k=2, E=4, d=256, h=1024, seed=16, drop_frac=0.0, empty_experts=(2,)),
+        # the permute's one-workgroup path (at most 64 chunks of 256 slots and 8192 table entries) at
+        # its boundary, one chunk past it, and with too many experts for its table
+        dict(T=8192, k=2, E=16, d=64, h=64, seed=17, drop_frac=0.1),
+        dict(T=8193, k=2, E=16, d=64, h=64, seed=18, drop_frac=0.1),
+        dict(T=2048, k=4, E=1024, d=64, h=64, seed=19, drop_frac=0.05),
     ]
     return cases
 
