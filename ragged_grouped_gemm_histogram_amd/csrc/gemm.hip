@@ -248,10 +248,10 @@ __device__ void build_problem_list(const GemmArgs& g, ProblemList<THREADS>& pl) 
 // Tile t -> (expert, m-tile, n-tile). Groups of GM consecutive m-tiles
 // sweep every n-tile before the next group starts, so tiles that run at the
 // same time share A rows and weight rows.
-template <int BM, int TILE_N, int THREADS, int GM = kGroupM>
+template <int BM, int TILE_N, int THREADS>
 __device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int total_mt, int E,
-                                                const ProblemList<THREADS>& pl) {
-  constexpr int kGroupM = GM;
+                                                const ProblemList<THREADS>& pl, int group_m = kGroupM) {
+  const int kGroupM = group_m;
   const int64_t group_span = (int64_t)kGroupM * n_tiles;
   const int64_t group = t / group_span;
   const int64_t in_group = t - group * group_span;
@@ -449,12 +449,14 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
   const int nk = (int)(g.K / BK);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // N-contiguous weights (the down projection): one m-tile per group, so the 32 consecutive tiles an XCD
-  // runs at once cover every n-tile of a few row tiles and most row tiles' A rows are fetched into one
-  // XCD's L2 only (1-2% faster than groups of eight on the zipf64, Qwen3-shaped and square workloads).
-  constexpr int kGroup = B_NMAJOR ? 1 : kGroupM;
+  // N-contiguous weights (the down projection) with at most 12 n-tiles: one m-tile per group, so the 32
+  // consecutive tiles an XCD runs at once cover every n-tile of a few row tiles and most row tiles' A rows
+  // are fetched into one XCD's L2 only (1-2% faster than groups of eight on the zipf64, Qwen3-shaped and
+  // square workloads, 8 and 12 n-tiles). With more n-tiles that window would hold one or two row tiles
+  // and no weight tile twice (16 n-tiles: 2% slower; 320: 18% slower), so groups of eight stay.
+  const int group_m = (B_NMAJOR && n_tiles <= 12) ? 1 : kGroupM;
   for (int64_t t = logical_worker(); t < total_tiles; t += gridDim.x) {
-    const TileCoord tc = tile_coord<C::BM, TILE_N, C::THREADS, kGroup>(t, n_tiles, total_mt, g.E, pl);
+    const TileCoord tc = tile_coord<C::BM, TILE_N>(t, n_tiles, total_mt, g.E, pl, group_m);
     const uint16_t* Wexp = g.W + (int64_t)tc.e * g.w_expert_stride;
 
     // Source of each lane's 16-byte chunk for k0 = 0, as a byte offset from a
