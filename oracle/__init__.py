@@ -19,13 +19,14 @@ Sources (the three web pages the method is taken from):
   blocks, int32 cumulative offsets, the inverse map used by the atomic-free
   unpermute, the gate-then-up weight layout.
 
-Numerics: every contraction is evaluated in float64 on bf16-valued operands
-(the products of two bf16 values are exact in float64 and sums of a few
-thousand of them keep ~40 bits of headroom), and results are rounded to bf16
-with round-to-nearest-even exactly where the method stores a bf16 tensor.
-``precision="f32"`` instead runs the per-expert loop in float32, the form in
-which the method states its accumulation; the test suite pins the two against
-each other within the float32 error bound.
+Numerics: the forward's per-expert loop runs in float32 on bf16-valued
+operands by default, the precision in which the method states its
+accumulation, and results are rounded to bf16 with round-to-nearest-even
+exactly where the method stores a bf16 tensor. ``precision="f64"`` runs the
+same loop in float64 (products of two bf16 values are exact there and sums of
+a few thousand keep ~40 bits of headroom); the test suite pins the two against
+each other within the float32 error bound. The backward's functions keep
+float64 as their default.
 """
 
 from .backward import (expert_backward, grouped_dgrad, grouped_wgrad, permute_backward, swiglu_backward,
@@ -44,6 +45,7 @@ from .moe import (
     permute_rows,
     route_histogram,
     stable_route_order,
+    swiglu_rows,
     tile_count,
     token_forward,
     unpermute,
@@ -72,6 +74,7 @@ __all__ = [
     "route_histogram",
     "stable_route_order",
     "swiglu_backward",
+    "swiglu_rows",
     "tile_count",
     "token_forward",
     "unpermute",

@@ -192,8 +192,8 @@ def expert_backward(dy_bits, x_bits, expert_ids, routing_w, w_ug_bits, w_down_bi
     M = int(offsets[-1])
     perm, inv = stable_route_order(ids, E, offsets)
     x_perm = permute_rows(x_bits, perm, M, k)
-    h_bits, y_perm = expert_forward(x_perm, offsets, w_ug_bits, w_down_bits)
-    u_bits = grouped_projection(x_perm, offsets, np.swapaxes(w_ug_bits, 1, 2))  # U_e = bf16(X_e W_ug[e]^T)
+    h_bits, y_perm = expert_forward(x_perm, offsets, w_ug_bits, w_down_bits, precision="f64")
+    u_bits = grouped_projection(x_perm, offsets, np.swapaxes(w_ug_bits, 1, 2), precision="f64")  # U_e = bf16(X_e W_ug[e]^T)
     dy_perm, d_rw = unpermute_backward(dy_bits, y_perm, inv, routing_w, T, k, M)
     dh = grouped_dgrad(dy_perm, offsets, w_down_bits, "in_out")
     dw_down = grouped_wgrad(h_bits, dy_perm, offsets, "in_out")

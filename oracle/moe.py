@@ -25,6 +25,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
   they are stored as bf16.
 * Routing weights are float32 [T, k], applied at scatter-back, not
   renormalised when a slot is dropped; a token with no kept slot gets y = 0.
+* Working precision: the forward's contractions, SiLU and the weighted sum
+  run in float32 on bf16-valued operands by default, the accumulation
+  precision the method names; ``precision="f64"`` runs the same loop in
+  float64, and the test suite pins the two against each other within the
+  float32 error bound.
 """
 
 from __future__ import annotations
@@ -127,28 +132,53 @@ def _silu(g: np.ndarray) -> np.ndarray:
         return g / (g.dtype.type(1) + np.exp(-g))
 
 
+def _swiglu_values(u_full: np.ndarray, h: int, ft) -> np.ndarray:
+    """SwiGLU of bf16-valued pre-activations: ``bf16(SiLU(g) * u)`` with g = U[:, :h], u = U[:, h:].
+
+    The gate block comes first (halo notes: gate_up chunked into gate, then
+    up); SiLU(g) is not rounded on its own. Returns a bf16-valued float64 array.
+    """
+    g = u_full[:, :h].astype(ft)
+    u = u_full[:, h:].astype(ft)
+    return round_to_bf16(_silu(g) * u)
+
+
 def _swiglu_expert(a: np.ndarray, w_ug: np.ndarray, w_down: np.ndarray, h: int, ft):
     """One expert, Eq 13: U = A W_ug^T, H = SwiGLU(U), Y = H W_down.
 
     ``a`` [m, d], ``w_ug`` [2h, d], ``w_down`` [h, d], all float arrays of
-    bf16 values in the working precision ``ft``. Returns (H, Y) as bf16-valued
-    float64 arrays.
+    bf16 values in the working precision ``ft``. Returns (H, Y, U) as
+    bf16-valued float64 arrays.
     """
     u_full = round_to_bf16(np.matmul(a, w_ug.T))  # [m, 2h]
-    g = u_full[:, :h].astype(ft)
-    u = u_full[:, h:].astype(ft)
-    hid = round_to_bf16(_silu(g) * u)  # [m, h]
+    hid = _swiglu_values(u_full, h, ft)  # [m, h]
     y = round_to_bf16(np.matmul(hid.astype(ft), w_down))  # [m, d]
-    return hid, y
+    return hid, y, u_full
 
 
-def expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision: str = "f64"):
+def swiglu_rows(u_bits, precision: str = "f32") -> np.ndarray:
+    """The activation step of Eq 13 alone: ``H = bf16(SiLU(U[:, :h]) * U[:, h:])``.
+
+    ``u_bits`` uint16 [rows, 2h] holds bf16 pre-activations, gate block first.
+    Used to hold a stored activation to the SwiGLU of the pre-activation it was
+    computed from. Returns uint16 [rows, h].
+    """
+    ft = _ftype(precision)
+    u = bf16_bits_to_f64(np.asarray(u_bits, dtype=np.uint16))
+    if u.ndim != 2 or u.shape[1] % 2:
+        raise ValueError(f"U must be [rows, 2h], got {u.shape}")
+    return f64_to_bf16_bits(_swiglu_values(u, u.shape[1] // 2, ft))
+
+
+def expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision: str = "f32", return_u: bool = False):
     """Grouped SwiGLU expert step over the sorted rows (Eq 13 per expert).
 
     For every expert with ``counts[e] > 0`` its own weights multiply exactly
     its own block of rows ``[offsets[e], offsets[e+1])``; empty experts do no
     arithmetic (grouped-GEMM essay: distinct parameters per expert, zero-row
-    experts need no matrix work). Returns ``(h_bits [M, h], y_perm_bits [M, d])``.
+    experts need no matrix work). Returns ``(h_bits [M, h], y_perm_bits [M, d])``,
+    and the bf16 pre-activation ``u_bits [M, 2h]`` (gate block, then up block)
+    as a third entry when ``return_u``.
     """
     ft = _ftype(precision)
     offsets = np.asarray(offsets).astype(np.int64)
@@ -161,6 +191,7 @@ def expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision: str 
     x_perm = np.asarray(x_perm_bits, dtype=np.uint16)
     h_out = np.zeros((M, h), dtype=np.uint16)
     y_out = np.zeros((M, d), dtype=np.uint16)
+    u_out = np.zeros((M, two_h), dtype=np.uint16) if return_u else None
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -168,13 +199,15 @@ def expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision: str 
         a = bf16_bits_to_f64(x_perm[lo:hi]).astype(ft)
         wug = bf16_bits_to_f64(w_ug_bits[e]).astype(ft)
         wdn = bf16_bits_to_f64(w_down_bits[e]).astype(ft)
-        hid, y = _swiglu_expert(a, wug, wdn, h, ft)
+        hid, y, u_full = _swiglu_expert(a, wug, wdn, h, ft)
         h_out[lo:hi] = f64_to_bf16_bits(hid)
         y_out[lo:hi] = f64_to_bf16_bits(y)
-    return h_out, y_out
+        if return_u:
+            u_out[lo:hi] = f64_to_bf16_bits(u_full)
+    return (h_out, y_out, u_out) if return_u else (h_out, y_out)
 
 
-def grouped_projection(a_bits, offsets, w_bits, precision: str = "f64") -> np.ndarray:
+def grouped_projection(a_bits, offsets, w_bits, precision: str = "f32") -> np.ndarray:
     """One grouped expert projection: ``Y[rows_e] = bf16(A[rows_e] @ W[e])`` per expert.
 
     The single-projection problem the OLMo report measures in Sec 9.6 (Figs 38
@@ -209,7 +242,7 @@ def grouped_projection(a_bits, offsets, w_bits, precision: str = "f64") -> np.nd
 # --------------------------------------------------------------------------
 
 
-def unpermute(y_perm_bits, inv, routing_w, T: int, k: int, precision: str = "f64") -> np.ndarray:
+def unpermute(y_perm_bits, inv, routing_w, T: int, k: int, precision: str = "f32") -> np.ndarray:
     """``y[t] = bf16(sum_j w[t,j] * y_perm[inv[t,j]])`` over kept slots, j ascending.
 
     halo notes: the scatter-back is a gather through the inverse map followed
@@ -247,20 +280,22 @@ class MoeOracleResult:
     h: np.ndarray  # uint16 [M, h]
     y_perm: np.ndarray  # uint16 [M, d]
     y: np.ndarray  # uint16 [T, d]
+    u: np.ndarray | None = None  # uint16 [M, 2h], the bf16 pre-activation, when asked for
 
     @property
     def M(self) -> int:
         return int(self.offsets[-1])
 
 
-def moe_expert_forward(x_bits, expert_ids, routing_w, w_ug_bits, w_down_bits, precision: str = "f64",
-                       with_gemm: bool = True) -> MoeOracleResult:
+def moe_expert_forward(x_bits, expert_ids, routing_w, w_ug_bits, w_down_bits, precision: str = "f32",
+                       with_gemm: bool = True, keep_u: bool = False) -> MoeOracleResult:
     """Routed expert forward: histogram, offsets, stable order, gather, Eq 13, unpermute.
 
     Shapes: ``x_bits`` uint16 [T, d], ``expert_ids`` int [T, k],
     ``routing_w`` float32 [T, k], ``w_ug_bits`` uint16 [E, 2h, d] (gate rows
     [0, h), up rows [h, 2h)), ``w_down_bits`` uint16 [E, h, d].
-    ``with_gemm=False`` stops after the gather (h, y_perm, y left empty).
+    ``with_gemm=False`` stops after the gather (h, y_perm, y left empty);
+    ``keep_u=True`` also returns the bf16 pre-activation U of every sorted row.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     ids = np.asarray(expert_ids)
@@ -275,12 +310,14 @@ def moe_expert_forward(x_bits, expert_ids, routing_w, w_ug_bits, w_down_bits, pr
     if not with_gemm:
         empty = np.zeros((0, 0), dtype=np.uint16)
         return MoeOracleResult(counts, offsets, perm, inv.reshape(T, k), x_perm, empty, empty, empty)
-    h_bits, y_perm = expert_forward(x_perm, offsets, w_ug_bits, w_down_bits, precision)
+    out = expert_forward(x_perm, offsets, w_ug_bits, w_down_bits, precision, return_u=keep_u)
+    h_bits, y_perm = out[0], out[1]
     y = unpermute(y_perm.reshape(M, d), inv, routing_w, T, k, precision)
-    return MoeOracleResult(counts, offsets, perm, inv.reshape(T, k), x_perm, h_bits, y_perm, y)
+    return MoeOracleResult(counts, offsets, perm, inv.reshape(T, k), x_perm, h_bits, y_perm, y,
+                           out[2] if keep_u else None)
 
 
-def token_forward(x_row_bits, ids_row, w_row, w_ug_bits, w_down_bits, precision: str = "f64") -> np.ndarray:
+def token_forward(x_row_bits, ids_row, w_row, w_ug_bits, w_down_bits, precision: str = "f32") -> np.ndarray:
     """The same step for one token: its kept slots' experts applied to its row.
 
     Rows are independent in Eq 13, so a token's output needs only its own row
@@ -298,7 +335,7 @@ def token_forward(x_row_bits, ids_row, w_row, w_ug_bits, w_down_bits, precision:
             continue
         wug = bf16_bits_to_f64(w_ug_bits[e]).astype(ft)
         wdn = bf16_bits_to_f64(np.asarray(w_down_bits, dtype=np.uint16)[e]).astype(ft)
-        _, y = _swiglu_expert(a, wug, wdn, h, ft)
+        _, y, _ = _swiglu_expert(a, wug, wdn, h, ft)
         acc = acc + ft(np.float32(w_row[j])) * y.astype(ft)
     return f64_to_bf16_bits(acc).reshape(d)
 

@@ -47,4 +47,4 @@ def workload(name: str):
 def oracle_result(name: str):
     wl = workload(name)
     say(f"[oracle] {name}: T={wl.T} k={wl.k} E={wl.E} d={wl.d} h={wl.h}")
-    return oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
+    return oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, keep_u=True)

@@ -108,6 +108,16 @@ def pin_printed_arithmetic(orc) -> None:
     # Eq 16 on the toy with one EP rank: 8 * ceil(floor(1.25 * 2.5) / 8) = 8 (derived)
     assert orc.capacity_eq16(1.25, 2.5, 1) == 8
     assert orc.capacity_eq16(1.25, 512, 1) == 640
+    # Eq 16 with several EP ranks, evaluated by hand. Two ranks, Mbar = 103.2: each rank's share
+    # floor(1.25 * 103.2 / 2) = floor(64.5) = 64 rows, already a multiple of 8, so C = 2 * 8 * 8 = 128
+    # (a ceiling in place of the floor gives 2 * 8 * ceil(65 / 8) = 144; aligning the undivided
+    # floor(129) gives 2 * 8 * 17 = 272; dropping the factor M_E gives 64).
+    assert orc.capacity_eq16(1.25, 103.2, 2) == 128
+    # Eight ranks, Mbar = 100: floor(15.625) = 15 rows per rank, aligned up to 16: C = 8 * 16 = 128.
+    assert orc.capacity_eq16(1.25, 100, 8) == 128
+    # One rank, a share that is not a multiple of 8: floor(1.25 * 13.6) = 17 -> 8 * ceil(17 / 8) = 24
+    # (the ceiling slip gives ceil(17.0) = 17 too, so this case checks the alignment step alone).
+    assert orc.capacity_eq16(1.25, 13.6, 1) == 24
     e18 = gd["eq18"]
     assert orc.entropy_deficit(np.full(16, 7)) == e18["uniform"]
     assert abs(orc.entropy_deficit(np.eye(16, dtype=int)[3] * 99) - e18["single_expert"]) < 1e-15

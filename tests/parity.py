@@ -22,14 +22,23 @@ RTOL = 1e-2
 REL_L2 = 1e-2
 REL_MAX = 1e-2
 
-# The stored SwiGLU activations H = bf16(SiLU(g) * u) are formed from two values
-# that were themselves rounded to bf16 (g and u, the halves of U). An fp32
-# accumulation order different from the reference's can leave g and u each one
-# bf16 step (at most 2^-7 relative) from the reference's, and H's own rounding
-# adds another step; where SiLU(g) is large (g > 0) the three add up to
-# 3 * 2^-7 relative. For g < 0 the relative sensitivity grows like |g| but
-# |SiLU(g)| < 0.28, so the absolute bound covers it. y keeps the contract bound.
-RTOL_H = 3 * 2.0**-7
+# The stored SwiGLU activations H = bf16(SiLU(g) * u) are not held to the oracle's H
+# directly with the elementwise bound: g and u are themselves bf16 roundings of fp32 sums
+# whose order differs between the kernel and the oracle, and a one-step flip in either is
+# amplified by SiLU's slope 1 + g(1 - sigmoid(g)) (up to about 1.28) before H is rounded
+# again. The check is split at U instead:
+#   * U (stored by the U-keeping launch, whose h_buf must equal the plain launch's bit for
+#     bit) is held to the oracle's U with the elementwise contract bound;
+#   * H is held to the oracle's SwiGLU of the GPU's own U. Both sides evaluate SiLU(g) * u
+#     in fp32 from the same bf16 g and u; the kernel's hardware exponential and reciprocal
+#     differ from the oracle's by a few fp32 ulps, which moves the bf16 rounding of H by one
+#     step only where the fp32 value lies within those few ulps of a rounding boundary:
+#     at most H_MAX_ULP steps, and (a few times 2^-24 against a bf16 step of 2^-8, about
+#     1e-4 of the elements at most) at least H_MIN_EXACT of the elements bit-identical
+#     (small outputs may hold up to H_MIN_FLIPS differing elements).
+H_MAX_ULP = 1
+H_MIN_EXACT = 0.999
+H_MIN_FLIPS = 4
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -98,3 +107,23 @@ def assert_fails(fn, *args, **kwargs) -> None:
     except AssertionError:
         return
     raise AssertionError("negative control was accepted by the comparison")
+
+
+def compare_swiglu_of_u(h_bits, h_from_u_bits, what: str = "h_buf vs SwiGLU(U)") -> dict:
+    """H against the SwiGLU of the same U: at most H_MAX_ULP bf16 steps apart, at least H_MIN_EXACT identical."""
+    h_bits = np.asarray(h_bits, dtype=np.uint16)
+    h_from_u_bits = np.asarray(h_from_u_bits, dtype=np.uint16)
+    if h_bits.shape != h_from_u_bits.shape:
+        raise AssertionError(f"{what}: shape {h_bits.shape} != {h_from_u_bits.shape}")
+    if h_bits.size == 0:
+        return {"n": 0}
+    u = ulp_diff(h_bits, h_from_u_bits)
+    exact = float(np.mean(u == 0))
+    stats = {"n": int(u.size), "max_ulp": int(u.max()), "exact_frac": exact}
+    if stats["max_ulp"] > H_MAX_ULP:
+        i = int(np.argmax(u.reshape(-1)))
+        raise AssertionError(f"{what}: {stats['max_ulp']} bf16 steps apart at flat index {i}")
+    flips = int((u != 0).sum())
+    if flips > max(H_MIN_FLIPS, (1.0 - H_MIN_EXACT) * u.size):
+        raise AssertionError(f"{what}: {flips} of {u.size} elements differ (only {exact:.5f} identical)")
+    return stats

@@ -1,11 +1,15 @@
 """HIP path against the oracle, through the C ABI, on an MI355X.
 
 Integer outputs (counts, offsets, perm[0, M), inv_map) and the permuted rows are
-compared bit for bit. bf16 outputs (h_buf and y_perm rows [0, M), y) are held
-to |got - ref| <= 1e-2 + 1e-2*|ref| plus the data-scaled guards in parity.py.
-The five named workloads run at full size in the launch configuration the
-benchmark times; small random cases cover empty experts, invalid ids, tails
-and degenerate sizes.
+compared bit for bit. bf16 outputs y_perm rows [0, M) and y are held to
+|got - ref| <= 1e-2 + 1e-2*|ref| plus the data-scaled guards in parity.py. The
+SwiGLU activations h_buf are checked through their pre-activation: U from the
+U-keeping launch (whose h_buf must equal the path's bit for bit) against the
+oracle's U with the same bound, and h_buf against the oracle's SwiGLU of that U
+within one bf16 step (parity.py states why). The oracle runs its per-expert
+loop in float32. The five named workloads run at full size in the launch
+configuration the benchmark times; small random cases cover empty experts,
+invalid ids, tails and degenerate sizes.
 """
 
 import numpy as np
@@ -15,7 +19,7 @@ import torch
 import oracle
 import ragged_grouped_gemm_histogram_amd as moe
 from gpu_util import DeviceInputs, bits, oracle_result, say, to_dev, to_dev_bf16, workload
-from parity import RTOL_H, assert_fails, compare_bf16
+from parity import assert_fails, compare_bf16, compare_swiglu_of_u
 from workloads import WORKLOADS, make_random
 
 pytestmark = pytest.mark.gpu
@@ -23,8 +27,8 @@ pytestmark = pytest.mark.gpu
 NAMES = list(WORKLOADS)
 
 
-def run_path(wl, sync=True, fused=False):
-    di = DeviceInputs(wl)
+def run_path(wl, sync=True, fused=False, di=None):
+    di = di or DeviceInputs(wl)
     y, p, h_buf, y_perm = moe.moe_expert_forward(di.x, di.ids, di.w, di.w_ug, di.w_down, fused_gather=fused)
     if sync:
         torch.cuda.synchronize()
@@ -41,13 +45,35 @@ def check_permute(p, ref, wl):
         np.testing.assert_array_equal(bits(p.x_perm)[:M], ref.x_perm)
 
 
-def check_all(wl, ref, y, p, h_buf, y_perm):
+def check_h_through_u(h_buf, u, ref_u, ref_h, M, what="h_buf"):
+    """U against the oracle's U (contract bound); h_buf against the oracle's SwiGLU of the GPU's own U
+    (one bf16 step); h_buf against the oracle's H under the data-scaled guards."""
+    ub = bits(u)[:M]
+    hb = bits(h_buf)[:M]
+    s_u = compare_bf16(ub, ref_u, f"U ({what})")
+    s_s = compare_swiglu_of_u(hb, oracle.swiglu_rows(ub), f"{what} vs SwiGLU(U)")
+    s_h = compare_bf16(hb, ref_h, what, elementwise=False)
+    say(f"  U {s_u}\n  {what} vs SwiGLU(own U) {s_s}\n  {what} vs oracle H {s_h}")
+
+
+def u_of_path(di, p, wl):
+    """U from the U-keeping launch on the path's sorted rows (x_perm rebuilt when the path fused the gather)."""
+    x_perm = p.x_perm if p.x_perm is not None else moe.moe_permute(di.x, di.ids, wl.E).x_perm
+    return moe.moe_gemm_up_swiglu_u(x_perm, p.offsets, di.w_ug)
+
+
+def check_all(wl, ref, y, p, h_buf, y_perm, di=None):
     check_permute(p, ref, wl)
     M = ref.M
-    s_h = compare_bf16(bits(h_buf)[:M], ref.h, "h_buf", rtol=RTOL_H)
+    di = di or DeviceInputs(wl)
+    h_u, u = u_of_path(di, p, wl)
+    torch.cuda.synchronize()
+    assert torch.equal(h_u[:M], h_buf[:M]), "the U-keeping launch's h_buf differs from the path's"
+    check_h_through_u(h_buf, u, ref.u, ref.h, M)
+    del h_u, u
     s_yp = compare_bf16(bits(y_perm)[:M], ref.y_perm, "y_perm")
     s_y = compare_bf16(bits(y), ref.y, "y")
-    say(f"  h_buf {s_h}\n  y_perm {s_yp}\n  y {s_y}")
+    say(f"  y_perm {s_yp}\n  y {s_y}")
     return s_y
 
 
@@ -57,9 +83,10 @@ def check_all(wl, ref, y, p, h_buf, y_perm):
 def test_named_workload_full_size(name, fused):
     wl = workload(name)
     say(f"[gpu] full path {name} fused_gather={fused}")
-    y, p, h_buf, y_perm = run_path(wl, fused=fused)
+    di = DeviceInputs(wl)
+    y, p, h_buf, y_perm = run_path(wl, fused=fused, di=di)
     ref = oracle_result(name)
-    check_all(wl, ref, y, p, h_buf, y_perm)
+    check_all(wl, ref, y, p, h_buf, y_perm, di)
 
 
 def _fuzz_cases():
@@ -117,9 +144,10 @@ FUZZ = _fuzz_cases()
 def test_random_cases(case):
     wl = make_random(**case)
     say(f"[gpu] random case {case}")
-    y, p, h_buf, y_perm = run_path(wl)
-    ref = oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down)
-    check_all(wl, ref, y, p, h_buf, y_perm)
+    di = DeviceInputs(wl)
+    y, p, h_buf, y_perm = run_path(wl, di=di)
+    ref = oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, keep_u=True)
+    check_all(wl, ref, y, p, h_buf, y_perm, di)
     # the down projection alone, from the GPU's own h_buf: its error without GEMM 1's roundings
     M = ref.M
     chained = oracle.grouped_projection(bits(h_buf)[:M], ref.offsets, wl.w_down)
@@ -240,8 +268,10 @@ def test_out_of_range_offsets_stay_in_bounds():
     bad = torch.tensor([-5, 25, 40, 10_000], dtype=torch.int32, device="cuda:0")
     say("[gpu] clamped offsets")
     h_buf, y_perm = moe.grouped_swiglu_expert(x_perm, bad, di.w_ug, di.w_down)
+    h_u, u = moe.moe_gemm_up_swiglu_u(x_perm, bad, di.w_ug)
     torch.cuda.synchronize()
+    assert torch.equal(h_u, h_buf)
     clamped = np.array([0, 25, 40, S], dtype=np.int32)  # what the device clamp makes of them
-    h_ref, yp_ref = oracle.expert_forward(bits(x_perm), clamped, wl.w_ug, wl.w_down)
-    compare_bf16(bits(h_buf), h_ref, "h_buf (clamped offsets)", rtol=RTOL_H)
+    h_ref, yp_ref, u_ref = oracle.expert_forward(bits(x_perm), clamped, wl.w_ug, wl.w_down, return_u=True)
+    check_h_through_u(h_buf, u, u_ref, h_ref, S, "h_buf (clamped offsets)")
     compare_bf16(bits(y_perm), yp_ref, "y_perm (clamped offsets)")

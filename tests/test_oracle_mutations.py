@@ -27,16 +27,47 @@ def _swiglu_variant(gate_up_swapped=False, round_u=True, use_up=True, transpose_
         act = g / (ft(1) + np.exp(-silu_sign * g))
         hid = round_to_bf16(act * u if use_up else act)
         wd = w_down.T if transpose_down else w_down
-        return hid, round_to_bf16(np.matmul(hid.astype(ft), wd))
+        return hid, round_to_bf16(np.matmul(hid.astype(ft), wd)), u_full
     return f
 
 
-def _expert_forward_shifted(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision="f64"):
+def _swiglu_values_sign(u_full, h, ft):
+    # the stand-alone activation step with SiLU's sign flipped (SiLU(-g) in place of SiLU(g))
+    g = u_full[:, :h].astype(ft)
+    u = u_full[:, h:].astype(ft)
+    return round_to_bf16(g / (ft(1) + np.exp(g)) * u)
+
+
+def _expert_forward_shifted(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision="f32", return_u=False):
     # wrong weight index: expert e multiplied by expert (e+1)'s weights
     E = w_ug_bits.shape[0]
-    return _orig_expert_forward(x_perm_bits, offsets, np.roll(w_ug_bits, -1, axis=0),
-                                np.roll(w_down_bits, -1, axis=0), precision) if E > 1 else \
-        _orig_expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision)
+    if E > 1:
+        w_ug_bits, w_down_bits = np.roll(w_ug_bits, -1, axis=0), np.roll(w_down_bits, -1, axis=0)
+    return _orig_expert_forward(x_perm_bits, offsets, w_ug_bits, w_down_bits, precision, return_u)
+
+
+def _eq16_ceil_inner(c, Mbar, M_E):
+    # Eq 16 with the inner floor taken as a ceiling
+    from fractions import Fraction
+    import math
+    inner = math.ceil(Fraction(str(c)) * Fraction(str(Mbar)) / int(M_E))
+    return int(M_E) * 8 * math.ceil(Fraction(inner, 8))
+
+
+def _eq16_rank_factor_dropped(c, Mbar, M_E):
+    # Eq 16 without the outer factor M_E (one rank's share returned as the capacity)
+    from fractions import Fraction
+    import math
+    inner = math.floor(Fraction(str(c)) * Fraction(str(Mbar)) / int(M_E))
+    return 8 * math.ceil(Fraction(inner, 8))
+
+
+def _eq16_share_undivided(c, Mbar, M_E):
+    # Eq 16 aligning c * Mbar itself instead of each rank's share of it
+    from fractions import Fraction
+    import math
+    inner = math.floor(Fraction(str(c)) * Fraction(str(Mbar)))
+    return int(M_E) * 8 * math.ceil(Fraction(inner, 8))
 
 
 _orig_expert_forward = om.expert_forward
@@ -66,7 +97,7 @@ def _offsets_inclusive(counts):
     return np.concatenate([c, c[-1:]]).astype(np.int32)
 
 
-def _unpermute_unweighted(y_perm_bits, inv, routing_w, T, k, precision="f64"):
+def _unpermute_unweighted(y_perm_bits, inv, routing_w, T, k, precision="f32"):
     return _orig_unpermute(y_perm_bits, inv, np.ones_like(np.asarray(routing_w)), T, k, precision)
 
 
@@ -78,12 +109,12 @@ def _truncate_bf16(x):
 _orig_projection = om.grouped_projection
 
 
-def _projection_shifted(a_bits, offsets, w_bits, precision="f64"):
+def _projection_shifted(a_bits, offsets, w_bits, precision="f32"):
     # wrong weight index: expert e multiplied by expert (e+1)'s weights
     return _orig_projection(a_bits, offsets, np.roll(np.asarray(w_bits), -1, axis=0), precision)
 
 
-def _projection_rows_shifted(a_bits, offsets, w_bits, precision="f64"):
+def _projection_rows_shifted(a_bits, offsets, w_bits, precision="f32"):
     # off-by-one segment: every expert's block starts one row late
     offs = np.asarray(offsets).astype(np.int64).copy()
     offs[1:-1] += 1
@@ -91,7 +122,7 @@ def _projection_rows_shifted(a_bits, offsets, w_bits, precision="f64"):
     return _orig_projection(a_bits, offs, w_bits, precision)
 
 
-def _projection_unrounded(a_bits, offsets, w_bits, precision="f64"):
+def _projection_unrounded(a_bits, offsets, w_bits, precision="f32"):
     # the stored Y left in a truncating conversion instead of round-to-nearest-even
     offsets = np.asarray(offsets).astype(np.int64)
     out = np.zeros((int(offsets[-1]), np.asarray(w_bits).shape[2]), dtype=np.uint16)
@@ -174,6 +205,10 @@ MUTATIONS = {
     "inclusive_offsets": [("exclusive_offsets", _offsets_inclusive)],
     "weights_ignored": [("unpermute", _unpermute_unweighted)],
     "truncating_rounding": [("round_to_bf16", _truncate_bf16)],
+    "swiglu_step_sign": [("_swiglu_values", _swiglu_values_sign)],
+    "eq16_ceil_inner": [("capacity_eq16", _eq16_ceil_inner)],
+    "eq16_rank_factor_dropped": [("capacity_eq16", _eq16_rank_factor_dropped)],
+    "eq16_share_undivided": [("capacity_eq16", _eq16_share_undivided)],
     "projection_wrong_expert": [("grouped_projection", _projection_shifted)],
     "projection_rows_shifted": [("grouped_projection", _projection_rows_shifted)],
     "projection_truncated": [("grouped_projection", _projection_unrounded)],
