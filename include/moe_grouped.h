@@ -71,7 +71,9 @@ typedef enum moe_status {
                                      tensor not 4-byte aligned                                  */
   MOE_ERR_WORKSPACE = 4,          /* workspace_bytes below the call's *_workspace_bytes()       */
   MOE_ERR_UNSUPPORTED_DEVICE = 5, /* the current HIP device is not gfx950, or no device         */
-  MOE_ERR_LAUNCH = 6              /* a HIP error was reported while launching                    */
+  MOE_ERR_LAUNCH = 6,             /* a HIP error was reported while launching                    */
+  MOE_ERR_TOO_LARGE = 7           /* moe_permute_noalloc only: E * ceil(T*k / 256) exceeds its
+                                     fixed table of MOE_PERMUTE_NOALLOC_TABLE_ENTRIES            */
 } moe_status;
 
 /* Bytes of device workspace moe_permute needs for T tokens, k slots per token
@@ -105,6 +107,26 @@ size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
 moe_status moe_permute(const uint16_t* x, const int32_t* expert_ids, int64_t T, int32_t k, int64_t d,
                        int32_t E, uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv_map, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_permute for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, results and stream semantics as
+ * moe_permute, without the workspace: the per-chunk histogram table lives in a
+ * fixed array of MOE_PERMUTE_NOALLOC_TABLE_ENTRIES int32 (4 MiB) in the
+ * library's own device memory, one per GPU, held until the process ends. Its
+ * address is resolved on a device's first call (that device current); the call
+ * never allocates, frees or synchronises.
+ *
+ * Limit: E * ceil(T*k / 256) <= MOE_PERMUTE_NOALLOC_TABLE_ENTRIES (for E = 64,
+ * up to 4,194,304 slots; for E = 1024, up to 262,144), else MOE_ERR_TOO_LARGE
+ * and nothing is launched. Every call on one GPU shares that GPU's table: calls
+ * whose executions overlap on one GPU (concurrent streams, or graphs replayed
+ * on several streams) race and give wrong results; calls ordered on one stream
+ * are safe. The table's contents from the previous call are never read. */
+#define MOE_PERMUTE_NOALLOC_TABLE_ENTRIES (1 << 20)
+moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* expert_ids, int64_t T, int32_t k, int64_t d,
+                               int32_t E, uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_map, hipStream_t stream);
 
 /* Grouped SwiGLU expert (OLMo report Eq 13 and Sec 9.2's device-scheduled
  * grouped GEMM). For every expert e with rows [offsets[e], offsets[e+1]):

@@ -29,6 +29,7 @@ _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c
 _SIGNATURES = {
     "moe_permute_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_permute_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "grouped_swiglu_expert": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_gemm_up_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "moe_gemm_up_swiglu_u": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -161,6 +162,33 @@ def moe_permute(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int, *, 
                                       _ptr(counts), _ptr(offsets),
                            _ptr(perm), _ptr(inv_map), _ptr(workspace), workspace.numel(), _stream(x)),
            "moe_permute")
+    return Permuted(x_perm, counts, offsets, perm, inv_map)
+
+
+def moe_permute_noalloc(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int, *, x_perm: torch.Tensor | None,
+                        counts: torch.Tensor, offsets: torch.Tensor, perm: torch.Tensor,
+                        inv_map: torch.Tensor) -> Permuted:
+    """moe_permute without a workspace, for callers that cannot allocate: the histogram table is the library's
+    fixed per-device array (at most ``E * ceil(T*k/256) <= 2**20`` entries). Every output is the caller's own
+    tensor, so this call allocates nothing; ``x_perm=None`` skips the row copy. Calls that overlap on one GPU
+    share the table and race."""
+    if x.dim() != 2 or expert_ids.dim() != 2:
+        raise ValueError("x must be [T, d] and expert_ids [T, k]")
+    T, d = x.shape
+    k = expert_ids.shape[1]
+    dev = x.device
+    _want(x, "x", torch.bfloat16, (T, d), dev)
+    _want(expert_ids, "expert_ids", torch.int32, (T, k), dev)
+    S, E = T * k, int(num_experts)
+    if x_perm is not None:
+        _want(x_perm, "x_perm", torch.bfloat16, (S, d), dev)
+    _want(counts, "counts", torch.int32, (E,), dev)
+    _want(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _want(perm, "perm", torch.int32, (S,), dev)
+    _want(inv_map, "inv_map", torch.int32, (T, k), dev)
+    _check(load_library().moe_permute_noalloc(_ptr(x) if x_perm is not None else None, _ptr(expert_ids), T, k, d,
+                                              E, _ptr(x_perm), _ptr(counts), _ptr(offsets), _ptr(perm),
+                                              _ptr(inv_map), _stream(x)), "moe_permute_noalloc")
     return Permuted(x_perm, counts, offsets, perm, inv_map)
 
 
@@ -452,7 +480,7 @@ def moe_expert_forward(x, expert_ids, routing_w, w_ug, w_down, fused_gather: boo
 __all__ = [
     "LIB_PATH", "MAX_EXPERTS", "MoeError", "Permuted", "grouped_swiglu_expert", "header_functions", "load_library",
     "grouped_swiglu_expert_gather", "moe_expert_forward", "moe_gemm_down", "moe_gemm_up_swiglu",
-    "moe_gemm_up_swiglu_gather", "moe_gemm_up_swiglu_u", "moe_permute", "moe_unpermute",
+    "moe_gemm_up_swiglu_gather", "moe_gemm_up_swiglu_u", "moe_permute", "moe_permute_noalloc", "moe_unpermute",
     "permute_workspace_bytes", "W_LAYOUTS", "moe_grouped_dgrad", "moe_grouped_wgrad", "moe_permute_backward", "wgrad_workspace_bytes",
     "moe_grouped_projection", "moe_swiglu_backward", "moe_expert_backward",
     "moe_unpermute_backward",

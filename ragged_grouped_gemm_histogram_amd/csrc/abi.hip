@@ -83,6 +83,29 @@ moe_status moe_permute(const uint16_t* x, const int32_t* expert_ids, int64_t T, 
                                  static_cast<int32_t*>(workspace), stream));
 }
 
+moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* expert_ids, int64_t T, int32_t k, int64_t d,
+                               int32_t E, uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_map, hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS || bad_width(d) || T > kMaxSlots / k) return MOE_ERR_BAD_SHAPE;
+  const int64_t S = T * k;
+  if ((int64_t)E * permute_chunks(S) > kStaticTableEntries) return MOE_ERR_TOO_LARGE;
+  if ((x_perm != nullptr && missing(x, T * d)) || missing(expert_ids, S) || missing(counts, E) ||
+      missing(offsets, E + 1) || missing(perm, S) || missing(inv_map, S))
+    return MOE_ERR_NULL_POINTER;
+  if (misaligned(x, 16) || misaligned(x_perm, 16) || misaligned(expert_ids, 4) || misaligned(counts, 4) ||
+      misaligned(offsets, 4) || misaligned(perm, 4) || misaligned(inv_map, 4))
+    return MOE_ERR_MISALIGNED;
+  const moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  int dev = -1;
+  int32_t* table = nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || static_table(dev, &table) != hipSuccess) return MOE_ERR_LAUNCH;
+  (void)hipGetLastError();
+  // Every table entry a call reads was written earlier in the same call (the histogram launch writes
+  // all E x chunks entries before the scan and the scatter read them), so nothing needs clearing.
+  return launched(launch_permute(x, expert_ids, T, k, d, E, x_perm, counts, offsets, perm, inv_map, table, stream));
+}
+
 moe_status moe_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug, int64_t cap_rows,
                               int64_t d, int64_t h, int32_t E, uint16_t* h_buf, hipStream_t stream) {
   moe_status st = check_gemm_shape(cap_rows, d, h, E);
@@ -309,6 +332,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than the call's *_workspace_bytes()";
     case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE: the current HIP device is not gfx950";
     case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: a kernel launch reported a HIP error";
+    case MOE_ERR_TOO_LARGE: return "MOE_ERR_TOO_LARGE: the call needs more than the fixed table of moe_permute_noalloc (E * ceil(T*k/256) > 2^20)";
   }
   return "unknown moe_status";
 }

@@ -49,6 +49,11 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int3
                           uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                           int32_t* table, hipStream_t stream);
 
+// Entries of the fixed per-device table behind moe_permute_noalloc (E * permute_chunks(T*k) int32
+// at most; 4 MiB per device), and its device address on device `dev`, which must be current.
+constexpr int64_t kStaticTableEntries = MOE_PERMUTE_NOALLOC_TABLE_ENTRIES;
+hipError_t static_table(int dev, int32_t** table);
+
 hipError_t launch_gemm_up_swiglu(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_ug,
                                  int64_t cap_rows, int64_t d, int64_t h, int32_t E, uint16_t* h_buf,
                                  hipStream_t stream);

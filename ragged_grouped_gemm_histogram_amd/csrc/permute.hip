@@ -18,7 +18,15 @@
 //   4. gather   x_perm[p] = x[perm[p] / k] for p < M, 16-byte vector copies
 // Integer work only; the result is independent of scheduling (bit-exact).
 
+#include <atomic>
+
 #include "common.h"
+
+// The per-chunk histogram table of moe_permute_noalloc, for callers that cannot allocate: a
+// fixed array in the library's own device memory. Each GPU holds its own copy at its own
+// address for as long as the process lives. In host code this name is only a stand-in for
+// the symbol: the device address comes from hipGetSymbolAddress (see static_table below).
+static __device__ __align__(256) int32_t scratch[moe::kStaticTableEntries];
 
 namespace moe {
 namespace {
@@ -308,7 +316,27 @@ int bits_for(int E) {
   return b;
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_table_addr[kMaxDevices];  // device address of `scratch`, per device
+
 }  // namespace
+
+hipError_t static_table(int dev, int32_t** table) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* p = g_table_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // First call on this device (the caller made it current): resolve the array's address on
+    // it once. Two threads may both resolve it; they store the same value.
+    void* addr = nullptr;
+    const hipError_t st = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (st != hipSuccess) return st;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<int32_t*>(addr);
+    g_table_addr[dev].store(p, std::memory_order_release);
+  }
+  *table = p;
+  return hipSuccess;
+}
 
 hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int32_t k, int64_t d, int32_t E,
                           uint16_t* x_perm, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,

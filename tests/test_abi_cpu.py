@@ -13,7 +13,7 @@ import torch
 
 import ragged_grouped_gemm_histogram_amd as moe
 
-OK, NULLP, SHAPE, ALIGN, WS, DEV, LAUNCH = range(7)
+OK, NULLP, SHAPE, ALIGN, WS, DEV, LAUNCH, TOO_LARGE = range(8)
 
 # The host-sanitizer test re-runs this file against a build whose host code carries
 # AddressSanitizer and UndefinedBehaviorSanitizer checks.
@@ -36,7 +36,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.moe_status_string(s).decode().startswith("MOE_")
     assert b"unknown" in lib.moe_status_string(99)
 
@@ -69,6 +69,33 @@ def permute(lib, T=4, k=2, d=8, E=4, x=FAKE, ids=FAKE, xp=FAKE, counts=FAKE, off
 ])
 def test_permute_validation(lib, kw, status):
     assert permute(lib, **kw) == status
+
+
+def permute_noalloc(lib, T=4, k=2, d=8, E=4, x=FAKE, ids=FAKE, xp=FAKE, counts=FAKE, offs=FAKE, perm=FAKE,
+                    inv=FAKE):
+    return lib.moe_permute_noalloc(x, ids, T, k, d, E, xp, counts, offs, perm, inv, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(E=0), SHAPE), (dict(E=1025), SHAPE), (dict(d=12), SHAPE),
+    (dict(T=2**31, k=1), SHAPE),
+    # the fixed table holds 2^20 entries: E * ceil(T*k / 256) beyond it is refused before anything else
+    (dict(T=70000, k=4, E=1024), TOO_LARGE), (dict(T=1 << 22, k=1, E=65), TOO_LARGE),
+    (dict(ids=None), NULLP), (dict(counts=None), NULLP), (dict(perm=None), NULLP), (dict(inv=None), NULLP),
+    (dict(x=None), NULLP), (dict(ids=FAKE + 2), ALIGN), (dict(xp=FAKE + 2), ALIGN),
+])
+def test_permute_noalloc_validation(lib, kw, status):
+    assert permute_noalloc(lib, **kw) == status
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid sizes with placeholder pointers: host without a GPU only")
+def test_permute_noalloc_limit_boundary(lib):
+    # exactly 2^20 entries (E = 64, 16384 chunks of 256 slots) passes validation; one slot more does not
+    T = 16384 * 256
+    assert permute_noalloc(lib, T=T, k=1, E=64) in (OK, DEV)
+    assert permute_noalloc(lib, T=T + 1, k=1, E=64) == TOO_LARGE
+    # no row copy asked for: x may be NULL
+    assert permute_noalloc(lib, x=None, xp=None) in (OK, DEV)
 
 
 def test_permute_empty_tensors_may_be_null(lib):
@@ -148,6 +175,7 @@ def test_unpermute_validation(lib, kw, status):
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour on a host without a GPU")
 def test_device_check_without_gpu(lib):
     assert permute(lib) == DEV
+    assert permute_noalloc(lib) == DEV
     assert gemm(lib, "moe_gemm_down") == DEV
     assert lib.moe_unpermute(FAKE, FAKE, FAKE, 4, 2, 8, FAKE, None) == DEV
 
