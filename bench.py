@@ -64,13 +64,201 @@ def algorithmic_bytes(T, k, M, d, h, nonempty, fused=True):
     return {"permute": permute, "gemm_up_swiglu": gemm1, "gemm_down": gemm2, "unpermute": unpermute}
 
 
+def entropy_deficit(counts) -> float:
+    """Eq 18 of the OLMo report (Sec 9.6): I_H = 1 - H(p) / log N_local with p_e = M_e / M, 0 log 0 = 0;
+    N_local counts every local expert, empty ones included; one expert, or no rows, gives 0."""
+    n = len(counts)
+    M = sum(int(c) for c in counts)
+    if n <= 1 or M == 0:
+        return 0.0
+    H = -sum((c / M) * math.log(c / M) for c in counts if c > 0)
+    return 1.0 - H / math.log(n)
+
+
+def capacity_eq16(c: float, mbar: float, ranks: int) -> int:
+    """Eq 16: C = M_E * 8 * ceil(floor(c * Mbar / M_E) / 8), the eight-row-aligned capacity per EP rank."""
+    from fractions import Fraction
+
+    inner = math.floor(Fraction(str(c)) * Fraction(mbar).limit_denominator(1 << 20) / ranks)
+    return ranks * 8 * math.ceil(Fraction(inner, 8))
+
+
+def histogram_stats(counts, tile_rows: int) -> dict:
+    """Load statistics of one routing (OLMo report Sec 9.2 and 9.6): I_H (Eq 18); the padded BMM's capacity
+    C = ceil(1.25 * M / E) (Fig 35 and the Fig 38 footnote), its padding fraction Eq 14 over the rows it
+    executes, E*C, counting only the rows that fit (rows past C are dropped), and the rows it drops; Eq 16's
+    capacity at c = 1.25 for one rank (this step runs without expert parallelism); the grouped GEMM's own
+    waste, the share of its row-tile slots that hold no row at the tile height it runs."""
+    counts = [int(c) for c in counts]
+    E, M = len(counts), sum(counts)
+    C = math.ceil(1.25 * M / E) if E else 0
+    kept = sum(min(c, C) for c in counts)
+    slots = sum(-(-c // tile_rows) * tile_rows for c in counts)
+    return {"I_H_eq18": entropy_deficit(counts), "M": M, "E": E, "nonempty_experts": sum(c > 0 for c in counts),
+            "max_rows": max(counts) if counts else 0, "min_nonempty_rows": min([c for c in counts if c > 0] or [0]),
+            "bmm_capacity_C": C, "rho_pad_eq14_at_C": (1 - kept / (E * C)) if E * C else 0.0,
+            "rho_pad_eq14_unclipped": (1 - M / (E * C)) if E * C else 0.0, "bmm_rows_dropped": M - kept,
+            "capacity_eq16_c1.25_one_rank": capacity_eq16(1.25, M / E, 1) if E else 0,
+            "grouped_tile_rows": tile_rows, "grouped_tile_padding": (1 - M / slots) if slots else 0.0}
+
+
+def gemm_tile_rows(M_cap: int, E: int, N_tiles: int, cus: int = 256) -> int:
+    """Row-tile height the grouped GEMM launch picks (256 when the mean block has >= 384 rows and its 256-row
+    tiles can occupy every CU, else 128); the rule the library applies on the host."""
+    return 256 if (M_cap >= 384 * E and (M_cap // 256 + E) * N_tiles >= cus) else 128
+
+
+class StepRun:
+    """Device buffers of one workload and its step: moe_permute (index maps only, or with the x_perm copy),
+    the gate/up GEMM with SwiGLU (gathering A rows through perm when fused), the down GEMM, moe_unpermute."""
+
+    def __init__(self, torch, moe, wl, dev, fused: bool):
+        import numpy as np
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        T, k, E, d, h = wl.T, wl.k, wl.E, wl.d, wl.h
+        S = T * k
+        self.wl, self.fused, self.moe = wl, fused, moe
+        self.x, self.w_ug, self.w_down = bf(wl.x), bf(wl.w_ug), bf(wl.w_down)
+        self.ids = torch.from_numpy(wl.expert_ids).to(dev)
+        self.rw = torch.from_numpy(wl.routing_w).to(dev)
+        self.x_perm = None if fused else torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+        self.h_buf = torch.empty((S, h), dtype=torch.bfloat16, device=dev)
+        self.y_perm = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+        self.counts = torch.empty((E,), dtype=torch.int32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        self.perm = torch.empty((S,), dtype=torch.int32, device=dev)
+        self.inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.ws = torch.empty((max(moe.permute_workspace_bytes(T, k, E), 4),), dtype=torch.uint8, device=dev)
+
+    def step(self, ev=None):
+        moe, wl = self.moe, self.wl
+        if ev is not None:
+            ev[0].record()
+        p = moe.moe_permute(self.x, self.ids, wl.E, x_perm=self.x_perm, counts=self.counts, offsets=self.offsets,
+                            perm=self.perm, inv_map=self.inv, workspace=self.ws, gather=not self.fused)
+        if ev is not None:
+            ev[1].record()
+        if self.fused:
+            moe.moe_gemm_up_swiglu_gather(self.x, p.perm, p.offsets, self.w_ug, wl.k, h_buf=self.h_buf)
+        else:
+            moe.moe_gemm_up_swiglu(p.x_perm, p.offsets, self.w_ug, h_buf=self.h_buf)
+        if ev is not None:
+            ev[2].record()
+        moe.moe_gemm_down(self.h_buf, p.offsets, self.w_down, y_perm=self.y_perm)
+        if ev is not None:
+            ev[3].record()
+        moe.moe_unpermute(self.y_perm, p.inv_map, self.rw, y=self.y)
+        if ev is not None:
+            ev[4].record()
+
+
+STAGES = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
+
+
+def time_step(torch, step, steps: int, warmup: int, graph: bool = True) -> dict:
+    """K eager steps with HIP events around every stage (per-stage times, each step's span on the stream), then,
+    unless graph is False, the same step captured once in a HIP graph and K replays, wall-clock timed. The
+    library allocates, synchronises and copies nothing, so its calls capture as they are; the kernels are the
+    same, the host launch gaps between them are gone."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    graph_ms, graph_note, replay = None, None, None
+    if graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    step()
+            torch.cuda.current_stream().wait_stream(side)
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            tg = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph_ms = (time.perf_counter() - tg) * 1e3 / steps
+            replay = g.replay
+        except Exception as exc:  # capture unavailable: the eager time stays the headline
+            graph_note = f"graph capture failed ({type(exc).__name__}: {exc}); eager launches reported"
+            torch.cuda.synchronize()
+    stage_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j, n in enumerate(STAGES)}
+    step_ev = sorted(ev[0].elapsed_time(ev[4]) for ev in events)  # each step's own span on the stream
+    step_events = {"mean_ms": sum(step_ev) / len(step_ev), "median_ms": step_ev[len(step_ev) // 2],
+                   "min_ms": step_ev[0], "max_ms": step_ev[-1]}
+    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "graph_note": graph_note, "replay": replay,
+            "stage_ms": stage_ms, "step_events": step_events}
+
+
+def stage_table(stage_ms: dict, algo: dict, M: int, d: int, h: int) -> dict:
+    """Per-stage mean time with its rate: GB/s of algorithmic bytes for the HBM-bound permutations, TFLOP/s for
+    the GEMMs (plus their algorithmic-byte rate, the bound of weight-streaming shapes)."""
+    gemm1_flops, gemm2_flops = 2 * M * d * (2 * h), 2 * M * h * d
+
+    def rate(b, ms):
+        return b / ms / 1e6 if ms > 0 else None
+
+    return {
+        "permute": {"ms": stage_ms["permute"], "GB/s": rate(algo["permute"], stage_ms["permute"])},
+        "gemm_up_swiglu": {"ms": stage_ms["gemm_up_swiglu"],
+                           "TFLOP/s": gemm1_flops / stage_ms["gemm_up_swiglu"] / 1e9,
+                           "algorithmic_GB/s": rate(algo["gemm_up_swiglu"], stage_ms["gemm_up_swiglu"])},
+        "gemm_down": {"ms": stage_ms["gemm_down"], "TFLOP/s": gemm2_flops / stage_ms["gemm_down"] / 1e9,
+                      "algorithmic_GB/s": rate(algo["gemm_down"], stage_ms["gemm_down"])},
+        "unpermute": {"ms": stage_ms["unpermute"], "GB/s": rate(algo["unpermute"], stage_ms["unpermute"])},
+    }
+
+
+def measure_config(torch, moe, name: str, dev, steps: int, warmup: int, fused: bool = True) -> dict:
+    """One named workload's step, timed as the headline is (graph replays; stages from eager events), with the
+    load statistics of its routing. A parity-test configuration, reported beside the headline."""
+    from workloads import WORKLOADS, make_workload
+
+    wl = make_workload(name)
+    run = StepRun(torch, moe, wl, dev, fused)
+    tm = time_step(torch, run.step, steps, warmup)
+    cnt = run.counts.cpu().tolist()
+    M = sum(cnt)
+    nonempty = sum(c > 0 for c in cnt)
+    ms = tm["graph_ms"] if tm["graph_ms"] is not None else tm["eager_ms"]
+    flops = useful_flops(M, wl.d, wl.h)
+    algo = algorithmic_bytes(wl.T, wl.k, M, wl.d, wl.h, nonempty, fused)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    t1 = gemm_tile_rows(wl.T * wl.k, wl.E, -(-wl.h // 128), cus)
+    t2 = gemm_tile_rows(wl.T * wl.k, wl.E, -(-wl.d // 256), cus)
+    out = {"workload": name, "seed": WORKLOADS[name][0], "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "h": wl.h,
+           "M": M, "ms_per_step": ms, "timing": "graph replays" if tm["graph_ms"] is not None else "eager",
+           "eager_ms_per_step": tm["eager_ms"], "useful_TFLOP/s": flops / (ms * 1e-3) / 1e12,
+           "pct_of_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "step_events": tm["step_events"], "stages": stage_table(tm["stage_ms"], algo, M, wl.d, wl.h),
+           "histogram": histogram_stats(cnt, t1), "down_tile_rows": t2}
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
 def file_sha(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def cpu_baseline(wl, tokens: int, min_seconds: float = 10.0):
-    """Time the oracle (as it stands) on the first `tokens` tokens of the workload."""
+def cpu_baseline(wl, tokens: int, min_seconds: float = 10.0, precision: str = "f32", max_runs: int = 5):
+    """Time the oracle (as it stands) on the first `tokens` tokens of the workload: its per-expert loop in
+    float32 (the form the method states), or float64 on request."""
     import numpy as np
 
     import oracle
@@ -84,9 +272,10 @@ def cpu_baseline(wl, tokens: int, min_seconds: float = 10.0):
     sl = slice(0, tokens)
     # whole runs until about 10 s of host work (at most 5 runs); the rate is the mean over them
     runs, total = 0, 0.0
-    while runs < 5 and (runs == 0 or total < min_seconds):
+    while runs < max_runs and (runs == 0 or total < min_seconds):
         t0 = time.perf_counter()
-        r = oracle.moe_expert_forward(wl.x[sl], wl.expert_ids[sl], wl.routing_w[sl], wl.w_ug, wl.w_down)
+        r = oracle.moe_expert_forward(wl.x[sl], wl.expert_ids[sl], wl.routing_w[sl], wl.w_ug, wl.w_down,
+                                      precision=precision)
         total += time.perf_counter() - t0
         runs += 1
     dt = total / runs
@@ -94,8 +283,9 @@ def cpu_baseline(wl, tokens: int, min_seconds: float = 10.0):
     return {"value": useful_flops(M, wl.d, wl.h) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": total, "runs": runs,
             "sample": f"first {tokens} of {wl.T} tokens of {wl.name} ({M} routed rows, all {wl.E} experts' weights), "
-                      f"float64 oracle, mean of {runs} runs ({total:.1f} s)", "host_cpus": len(os.sched_getaffinity(0)),
-            "numpy": np.__version__}
+                      f"{'float32' if precision == 'f32' else 'float64'} oracle (per-expert loop), mean of {runs} "
+                      f"runs ({total:.1f} s)", "host_cpus": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "precision": precision}
 
 
 def summarize_telemetry(samples, t0: float, t1: float, settle: float = 0.25):
@@ -235,7 +425,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="zipf64", choices=["toy", "edge", "qwen3_30b", "zipf64", "square"])
+    ap.add_argument("--config", default="zipf64", choices=["toy", "edge", "qwen3_30b", "zipf64", "square", "zipf64_top8"])
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other named workloads (reported under 'configs' beside the headline)")
     ap.add_argument("--no-variants", action="store_true", help="skip the padded-BMM and per-expert-loop variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0: all T tokens)")
@@ -272,111 +464,27 @@ def main(argv=None):
     if args.sweep:
         print(json.dumps(SWEEPS[args.sweep](torch, moe, dev, args.sweep_warmup, args.sweep_samples)))
         return 0
+    fused = not args.unfused
     wl = make_workload(args.config)
     T, k, E, d, h = wl.T, wl.k, wl.E, wl.d, wl.h
     S = T * k
-
-    def bf(a):
-        import numpy as np
-
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x, w_ug, w_down = bf(wl.x), bf(wl.w_ug), bf(wl.w_down)
-    ids = torch.from_numpy(wl.expert_ids).to(dev)
-    rw = torch.from_numpy(wl.routing_w).to(dev)
-    fused = not args.unfused
-    x_perm = None if fused else torch.empty((S, d), dtype=torch.bfloat16, device=dev)
-    h_buf = torch.empty((S, h), dtype=torch.bfloat16, device=dev)
-    y_perm = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
-    counts = torch.empty((E,), dtype=torch.int32, device=dev)
-    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-    perm = torch.empty((S,), dtype=torch.int32, device=dev)
-    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
-    ws = torch.empty((max(moe.permute_workspace_bytes(T, k, E), 4),), dtype=torch.uint8, device=dev)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        p = moe.moe_permute(x, ids, E, x_perm=x_perm, counts=counts, offsets=offsets, perm=perm, inv_map=inv,
-                            workspace=ws, gather=not fused)
-        if ev is not None:
-            ev[1].record()
-        if fused:
-            moe.moe_gemm_up_swiglu_gather(x, p.perm, p.offsets, w_ug, k, h_buf=h_buf)
-        else:
-            moe.moe_gemm_up_swiglu(p.x_perm, p.offsets, w_ug, h_buf=h_buf)
-        if ev is not None:
-            ev[2].record()
-        moe.moe_gemm_down(h_buf, p.offsets, w_down, y_perm=y_perm)
-        if ev is not None:
-            ev[3].record()
-        moe.moe_unpermute(y_perm, p.inv_map, rw, y=y)
-        if ev is not None:
-            ev[4].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Timed region: exactly K steps, events bracket every stage on the launch stream.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    eager_ms = elapsed * 1e3 / args.steps
-    graph_ms, graph_note = None, None
-    replay = None
-    if not args.eager:
-        # The same step captured once in a HIP graph (the library allocates, synchronises and copies
-        # nothing, so its calls capture as they are), then exactly K replays timed like the eager
-        # steps: the kernels are identical, the host launch gaps between them are gone.
-        try:
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(g, stream=side):
-                    step()
-            torch.cuda.current_stream().wait_stream(side)
-            for _ in range(args.warmup):
-                g.replay()
-            torch.cuda.synchronize()
-            tg = time.perf_counter()
-            for _ in range(args.steps):
-                g.replay()
-            torch.cuda.synchronize()
-            graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
-            replay = g.replay
-        except Exception as exc:  # capture unavailable: the eager time stays the headline
-            graph_note = f"graph capture failed ({type(exc).__name__}: {exc}); eager launches reported"
-            torch.cuda.synchronize()
+    run = StepRun(torch, moe, wl, dev, fused)
+    x, ids, rw, w_ug, w_down = run.x, run.ids, run.rw, run.w_ug, run.w_down
+    x_perm, y_perm, counts, offsets, inv, ws = run.x_perm, run.y_perm, run.counts, run.offsets, run.inv, run.ws
+    tm = time_step(torch, run.step, args.steps, args.warmup, graph=not args.eager)
+    eager_ms, graph_ms, graph_note, replay = tm["eager_ms"], tm["graph_ms"], tm["graph_note"], tm["replay"]
+    stage_ms, step_events = tm["stage_ms"], tm["step_events"]
 
     M = int(offsets[-1].item())
     nonempty = int((counts > 0).sum().item())
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     # Clock and power during about 1.5 s of the headline step back to back (after the timed region).
-    telemetry = None if args.no_telemetry else steady_telemetry(torch, replay or step, ms_per_step)
+    telemetry = None if args.no_telemetry else steady_telemetry(torch, replay or run.step, ms_per_step)
     flops = useful_flops(M, d, h)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    names = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
-    stage_ms = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
-    step_ev = sorted(ev[0].elapsed_time(ev[4]) for ev in events)  # each step's own span on the stream
-    step_events = {"mean_ms": sum(step_ev) / len(step_ev), "median_ms": step_ev[len(step_ev) // 2],
-                   "min_ms": step_ev[0], "max_ms": step_ev[-1]}
     algo = algorithmic_bytes(T, k, M, d, h, nonempty, fused)
     gemm1_flops = 2 * M * d * (2 * h)
-    gemm2_flops = 2 * M * h * d
-    stages = {
-        "permute": {"ms": stage_ms["permute"], "GB/s": algo["permute"] / stage_ms["permute"] / 1e6},
-        "gemm_up_swiglu": {"ms": stage_ms["gemm_up_swiglu"],
-                           "TFLOP/s": gemm1_flops / stage_ms["gemm_up_swiglu"] / 1e9},
-        "gemm_down": {"ms": stage_ms["gemm_down"], "TFLOP/s": gemm2_flops / stage_ms["gemm_down"] / 1e9},
-        "unpermute": {"ms": stage_ms["unpermute"], "GB/s": algo["unpermute"] / stage_ms["unpermute"] / 1e6},
-    }
+    stages = stage_table(stage_ms, algo, M, d, h)
 
     # Roofline of the dominant kernel: the gate/up projection with fused SwiGLU (two thirds of the FLOPs).
     g1_ms = stage_ms["gemm_up_swiglu"]
@@ -409,8 +517,25 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu_baseline:
-        tokens = args.cpu_tokens or T
-        cpu = cpu_baseline(wl, min(tokens, T))
+        tokens = min(args.cpu_tokens or T, T)
+        cpu = cpu_baseline(wl, tokens)  # the float32 per-expert loop, about 10 s of host work
+        # the same oracle in float64, one run, for reference
+        f64 = cpu_baseline(wl, tokens, min_seconds=0.0, precision="f64", max_runs=1)
+        cpu["f64_oracle"] = {key: f64[key] for key in ("value", "unit", "cores", "seconds", "runs", "sample")}
+
+    # Load statistics of the headline routing, and the other named workloads timed the same way.
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    hist = histogram_stats(counts.cpu().tolist(), gemm_tile_rows(S, E, -(-h // 128), cus))
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for name in [n for n in WORKLOADS if n != wl.name]:
+            _progress(f"config {name}")
+            try:
+                configs[name] = measure_config(torch, moe, name, dev, steps=args.steps, warmup=args.warmup,
+                                               fused=fused)
+            except Exception as exc:  # one failed configuration is reported, not fatal to the headline
+                configs[name] = {"error": f"{type(exc).__name__}: {exc}"}
 
     out = {
         "metric": METRIC,
@@ -437,8 +562,10 @@ def main(argv=None):
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "histogram": hist,
         "variants": variants,
         "telemetry": telemetry,
+        "configs": configs,
     }
     print(json.dumps(out))
     return 0
@@ -676,11 +803,18 @@ def sweep_capacity(torch, moe, dev, warmup, samples):
         del pad, out
         _progress(f"capacity sweep: M={M} grouped {g['mean_ms']:.4f} ms, bmm {b['mean_ms']:.4f} ms")
     cross = next((p["M"] for p in points if p["bmm_over_grouped_time"] > 1.0), None)
+    # the stable crossover: the smallest M from which the grouped projection is faster at every larger M too
+    stable = None
+    for p in reversed(points):
+        if p["bmm_over_grouped_time"] <= 1.0:
+            break
+        stable = p["M"]
     return {"metric": "useful TFLOP/s of one grouped projection vs padded BMM at 1.25x capacity, across M",
             "sweep": "capacity", "unit": "TFLOP/s", "data": "synthetic", "dtype": "bf16",
             "config": {"workload": "capacity sweep", "E": E, "d": dim, "h": dim, "capacity_factor": 1.25,
                        "warmup": warmup, "samples": samples, "kernel": "moe_gemm_down", "bmm": "torch.bmm"},
-            "first_M_grouped_faster": cross, "gate_overruns": timer.gate_overruns, "points": points}
+            "first_M_grouped_faster": cross, "stable_crossover_M": stable, "gate_overruns": timer.gate_overruns,
+            "points": points}
 
 
 def sweep_decomposition(torch, moe, dev, warmup, samples):

@@ -69,3 +69,35 @@ def test_energy_average_power_picks_the_timestamp_unit():
         watts, secs = bench.energy_average_power(e0, e1, host_seconds=2.05)
         assert secs == pytest.approx(2.0) and watts == pytest.approx(1350.0, rel=1e-6)
     assert bench.energy_average_power(e0, dict(e0), 1.0) == (None, None)  # no energy counted
+
+
+def test_histogram_statistics_agree_with_the_oracle():
+    # bench.py carries its own copies of Eq 14, 16 and 18 (it may not use the oracle outside its CPU-baseline leg)
+    import numpy as np
+
+    import oracle
+    from workloads import make_workload
+
+    for counts in ([1, 4, 3, 2], [0, 7, 0, 7], [5], [19346, 8274, 0, 133, 1], list(range(64))):
+        assert bench.entropy_deficit(counts) == pytest.approx(oracle.entropy_deficit(np.array(counts)), abs=1e-12)
+    for c, mbar, ranks in ((1.25, 2.5, 1), (1.25, 512, 1), (1.25, 103.2, 2), (1.25, 100, 8), (1.25, 1024.0, 1)):
+        assert bench.capacity_eq16(c, mbar, ranks) == oracle.capacity_eq16(c, mbar, ranks)
+    wl = make_workload("toy")
+    st = bench.histogram_stats(np.bincount(wl.expert_ids.reshape(-1), minlength=4).tolist(), tile_rows=2)
+    # Figs 35-37: C = 4, 16 rows executed, rho_pad = 0.375, no row past C; 12 tile slots hold 10 rows at 2 rows
+    assert st["bmm_capacity_C"] == 4 and st["rho_pad_eq14_at_C"] == 0.375 and st["bmm_rows_dropped"] == 0
+    assert st["rho_pad_eq14_unclipped"] == 0.375 and st["capacity_eq16_c1.25_one_rank"] == 8
+    assert st["grouped_tile_padding"] == pytest.approx(1 - 10 / 12)
+    assert st["I_H_eq18"] == pytest.approx(oracle.entropy_deficit(np.array([1, 4, 3, 2])))
+    # an overflowing expert: rows past C are dropped and Eq 14 counts only the rows that fit
+    st = bench.histogram_stats([10, 0, 0, 2], tile_rows=8)  # C = ceil(1.25 * 12 / 4) = 4; 4 + 2 rows fit
+    assert st["bmm_capacity_C"] == 4 and st["bmm_rows_dropped"] == 6
+    assert st["rho_pad_eq14_at_C"] == pytest.approx(1 - 6 / 16)
+
+
+def test_tile_height_rule():
+    # zipf64: 65,536 slots over 64 experts, 6 gate/up column tiles -> 256-row tiles; Qwen3-shaped: 128
+    assert bench.gemm_tile_rows(65536, 64, 6) == 256
+    assert bench.gemm_tile_rows(32768, 128, 6) == 128
+    # the edge workload: blocks are large, but its 256-row tiles could not occupy 256 CUs
+    assert bench.gemm_tile_rows(4096, 8, 3) == 128

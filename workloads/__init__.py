@@ -19,7 +19,10 @@ Qwen3-30B-A3B (hidden 2048, expert intermediate 768, 128 experts, top-8 over
 share of an expert-parallel layer with a Zipf-skewed load (OLMo report,
 Sec 9.6 on concentrated histograms), and square experts with d = h = 2880 (so
 K % 128 = 64 on both projections; halo notes, the K-tail case) with 5% of
-dispatch slots set to -1.
+dispatch slots set to -1. The 64-expert share draws each slot independently,
+so a token may send two slots to one expert and one expert may receive more
+than T rows; ``zipf64_top8`` is the same layer with eight distinct experts per
+token, the way a top-k router picks them.
 """
 
 from __future__ import annotations
@@ -139,6 +142,23 @@ def _zipf64(seed):
                    {"empty_experts": sorted(relabel[ZIPF_RANKS:].tolist())})
 
 
+def _zipf64_top8(seed):
+    rng = np.random.default_rng(seed)
+    T, k, E, d, h = 8192, 8, 64, 2048, 768
+    r = np.arange(1, ZIPF_RANKS + 1, dtype=np.float64)
+    logp = -ZIPF_S * np.log(r)
+    # k distinct ranks per token, drawn without replacement with probabilities proportional to
+    # r^-1.2 (Gumbel-top-k: the k largest of log p_r + Gumbel noise), as a top-k router picks them
+    keys = logp[None, :] + rng.gumbel(size=(T, ZIPF_RANKS))
+    rank = np.argsort(-keys, axis=1, kind="stable")[:, :k]
+    relabel = rng.permutation(E).astype(np.int32)
+    ids = relabel[rank]
+    w = _softmax_rows(rng.standard_normal((T, k), dtype=np.float32))
+    return _finish(rng, "zipf64_top8", T, k, E, d, h, ids, w, 1.0, 0.02,
+                   "64-expert share of an EP layer, 8192 tokens x top-8 distinct experts, Zipf(1.2) over 60 ranks",
+                   {"empty_experts": sorted(relabel[ZIPF_RANKS:].tolist())})
+
+
 def _square(seed):
     rng = np.random.default_rng(seed)
     T, k, E, d, h = 8192, 4, 16, 2880, 2880
@@ -158,11 +178,13 @@ WORKLOADS = {
     "qwen3_30b": (3, _qwen3_30b),
     "zipf64": (4, _zipf64),
     "square": (5, _square),
+    # the zipf64 layer with a top-8 router's distinct experts per token (no expert above T rows)
+    "zipf64_top8": (6, _zipf64_top8),
 }
 
 
 def make_workload(name: str, seed: int | None = None) -> Workload:
-    """One of the five named workloads; the default seed is its index 1..5."""
+    """One of the named workloads; the default seed is its index (1..5 for the five, 6 for zipf64_top8)."""
     idx, fn = WORKLOADS[name]
     return fn(idx if seed is None else seed)
 
