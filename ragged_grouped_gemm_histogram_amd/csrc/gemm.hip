@@ -296,6 +296,21 @@ __device__ __forceinline__ int b_block_row(int wn, int fn) {
 // exponential and reciprocal (a few fp32 ulps, far below the bf16 rounding of the result).
 __device__ __forceinline__ float swiglu(float gv, float uv) { return gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv; }
 
+// threadIdx.x, through an opaque register move when OPAQUE: the epilogues' LDS and global
+// addresses are fixed per lane, so the compiler otherwise computes them once before the tile
+// loop and keeps them (about 60 registers) live through every main loop. The 256-row tiles with
+// a plain (256-column) output need those registers for the second fragment set, and the
+// U-keeping and weight-gradient launches to avoid spilling; the other tiles are faster with the
+// addresses kept.
+template <bool OPAQUE>
+__device__ __forceinline__ int epilogue_tid() {
+  int tid = threadIdx.x;
+  if constexpr (OPAQUE) asm volatile("" : "+v"(tid));
+  return tid;
+}
+template <class C>
+constexpr bool kOpaqueEpilogue = !C::GATED && C::BM == 256;
+
 // Registers -> bf16 tile in LDS (swizzled 16-byte chunks) -> global. For the
 // gated projection, SwiGLU is applied here: g and u are rounded to bf16 first,
 // then SiLU(g) * u is evaluated in fp32 with the hardware exponential and
@@ -306,7 +321,7 @@ template <class C>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsigned char* smem, const GemmArgs& g,
                                          const TileCoord& tc) {
   constexpr int BM = C::BM, BN = C::BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = epilogue_tid<kOpaqueEpilogue<C>>(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   unsigned char* ot = smem;  // [BM][OUTW] bf16
   constexpr int OUT_ROW_BYTES = C::OUTW * 2;
@@ -382,7 +397,7 @@ __device__ __forceinline__ void epilogue_save_u(const f32x16 (&acc)[C::FM][C::FN
   constexpr int BM = C::BM, BN = C::BN;
   constexpr int U_CPR = BN / 8, U_ROW_BYTES = BN * 2, HALF = U_CPR / 2;
   static_assert(BM * U_ROW_BYTES <= C::LDS_BYTES, "U tile must fit in the stage buffers");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = epilogue_tid<true>(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int half_lane = lane >> 5;
   unsigned char* ut = smem;  // [BM][BN] bf16
@@ -585,44 +600,41 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         for (int i = 0; i < C::FM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
     };
-    // Stage kt is complete for this wave once only the later stages already
-    // issued are still in flight; after the barrier it is complete for every
-    // wave, and every wave has finished reading the stage before it.
-    // The next slice's fragments are read during the current slice's MFMAs when
-    // registers allow; the 256x256 tiles with a plain (256-column) output have
-    // no room for the second set and read each slice just before its MFMAs
-    // (the other wave on the SIMD covers the wait).
-    constexpr bool kPrefetch = !((B_NMAJOR || !C::GATED) && C::FM * C::FN >= 8);
-    // With fragment prefetch the hand-off waits through the compiler's own s_waitcnt and the
-    // last stage is peeled (see stage_body): the stage's MFMAs after the hand-off then wait for
-    // nothing (1-3% faster on the zipf64, square and Qwen3-shaped workloads, bit-identical).
-    // The loop without prefetch keeps the opaque wait: there the compiler's own bookkeeping
-    // made the zipf64 down projection 2% slower.
-    constexpr bool kExact = kPrefetch;
+    // The next slice's fragments are read during the current slice's MFMAs (two register
+    // sets, `load_frags` into the set the MFMAs do not use). The 256x256 tiles with a plain
+    // (256-column) output fit the second set only with their epilogue addresses kept out of the
+    // main loop (kOpaqueEpilogue); there it makes the down projection 2% (zipf64) and 5%
+    // (square) faster than reading each slice just before its MFMAs, bit-identical.
+    //
+    // Stage kt is complete for this wave once only the later stages already issued are still
+    // in flight; after the barrier it is complete for every wave, and every wave has finished
+    // reading the stage before it. The hand-off waits through the compiler's own s_waitcnt and
+    // the last stage is peeled (see stage_body): the stage's MFMAs after the hand-off then wait
+    // for nothing (1-3% faster on the zipf64, square and Qwen3-shaped workloads, bit-identical).
     auto wait_stage = [&](int kt) {
       const int ahead = min(nk - 1, kt + NST - 2) - kt;  // stages issued after kt, still allowed in flight
-      if (NST >= 4 && ahead >= 2) wait_vmcnt_lds<(NST >= 4 ? 2 : 0) * OPS, kExact>();
-      else if (NST >= 3 && ahead >= 1) wait_vmcnt_lds<(NST >= 3 ? 1 : 0) * OPS, kExact>();
-      else wait_vmcnt_lds<0, kExact>();
+      if (NST >= 4 && ahead >= 2) wait_vmcnt_lds<(NST >= 4 ? 2 : 0) * OPS, true>();
+      else if (NST >= 3 && ahead >= 1) wait_vmcnt_lds<(NST >= 3 ? 1 : 0) * OPS, true>();
+      else wait_vmcnt_lds<0, true>();
       bare_barrier();
     };
 
-    // Waves w and w+4 share a SIMD. With fragment prefetch and a 2-slot ring, waves 4..7 issue
-    // their share of a stage's loads one slice after waves 0..3 (at the start of the next
-    // stage instead of at the hand-off): when both waves of a SIMD issue eight wave loads at
-    // once, both can stall on load issue while neither issues MFMAs. Their loads still have
-    // three of the four slices to land (issuing them two slices late instead was 10% slower).
-    // Bit-identical results; the 256-row gate/up GEMM 2% faster on the zipf64 and square workloads.
-    // The launch that also keeps U has no registers to spare for it (the compiler spills).
-    const bool late_issue = kPrefetch && !SAVE_U && NST == 2 && C::NWAVES == 8 && wave >= 4;
+    // Waves w and w+4 share a SIMD. With a 2-slot ring, waves 4..7 issue their share of a
+    // stage's loads one slice after waves 0..3 (at the start of the next stage instead of at
+    // the hand-off): when both waves of a SIMD issue eight wave loads at once, both can stall on
+    // load issue while neither issues MFMAs. Their loads still have three of the four slices to
+    // land (issuing them two slices late instead was 10% slower). Bit-identical results; the
+    // 256-row gate/up GEMM 2% faster on the zipf64 and square workloads, the down projection 2%
+    // (zipf64) and 4% (square). The launch that also keeps U has no registers to spare for it
+    // (the compiler spills).
+    const bool late_issue = !SAVE_U && NST == 2 && C::NWAVES == 8 && wave >= 4;
     // Both slots of a 2-slot ring are free at the tile start: fill them and wait for the first
     // only, so the second has a whole stage more to land (0.5-1.5% faster, bit-identical).
-    constexpr bool kStart2 = NST == 2;
-    if constexpr (kStart2) {
+    if constexpr (NST == 2) {
       issue(0);
       if (nk > 1) {
         issue(1);
-        wait_vmcnt_lds<OPS, kExact>();
+        wait_vmcnt_lds<OPS, true>();
         bare_barrier();
       } else {
         wait_stage(0);
@@ -633,33 +645,26 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         if (s < nk) issue(s);
       wait_stage(0);
     }
-    if constexpr (kPrefetch) load_frags(0, 0, 0);
-    constexpr bool kPeel = kExact;
-    // One stage of the main loop; `last_c` marks the peeled last stage (no hand-off), and in the
-    // peeled loop every other stage hands off unconditionally, so no branch merges a path with
-    // pending fragment reads into one without them (the compiler's wait bookkeeping stays exact).
+    load_frags(0, 0, 0);
+    // One stage of the main loop; `last_c` marks the peeled last stage (no hand-off). Every
+    // other stage hands off unconditionally, so no branch merges a path with pending fragment
+    // reads into one without them (the compiler's wait bookkeeping stays exact).
     auto stage_body = [&](int kt, auto last_c) {
       constexpr bool kLast = decltype(last_c)::value;
-      const bool next = kLast ? false : (kPeel ? true : kt + 1 < nk);
       // The slot stage kt+NST-1 fills held stage kt-1, which every wave finished
       // reading before the barrier that made stage kt visible.
       // With a 3-slot ring (128-row tiles) the next stage's loads are spread over the four
-      // slices; the 2-slot ring issues them a stage ahead (with fragment prefetch, right
-      // after that barrier, inside the previous stage's last slice; the second wave of
-      // each SIMD one slice later, see late_issue).
+      // slices; the 2-slot ring issues them a stage ahead (right after that barrier, inside the
+      // previous stage's last slice; the second wave of each SIMD one slice later, see
+      // late_issue; stage 1 at the tile start).
       constexpr int kParts = NST >= 3 ? BK / 16 : 1;
       const bool more = kt + NST - 1 < nk;
       const int slot = kt % NST;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int cur = ks & 1;
-        if (more && ks < kParts && (!kPrefetch || NST > 2 || kt == 0 || late_issue) && !(kStart2 && kt == 0))
-          issue_part(kt + NST - 1, ks, kParts);
-        if constexpr (!kPrefetch) {
-          load_frags(0, slot, ks);
-          mfmas(0);
-          if (ks + 1 == BK / 16 && next) wait_stage(kt + 1);
-        } else if (ks + 1 < BK / 16) {
+        if (more && ks < kParts && (NST > 2 || (late_issue && kt > 0))) issue_part(kt + NST - 1, ks, kParts);
+        if (ks + 1 < BK / 16) {
           load_frags(cur ^ 1, slot, ks + 1);
           mfmas(cur);
           interleave_reads<C::FM * C::FN, C::FM + (B_NMAJOR ? 2 : 1) * C::FN>();
@@ -669,7 +674,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
           // the next stage's first slice) so that its MFMAs cover the barrier
           // and the read latency. The MFMAs stay outside the branch so the
           // accumulators keep one register assignment.
-          if (next) {
+          if constexpr (!kLast) {
             wait_stage(kt + 1);
             if (NST == 2 && kt + 2 < nk && !late_issue) issue(kt + 2);
             load_frags(cur ^ 1, (kt + 1) % NST, 0);
@@ -678,12 +683,8 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         }
       }
     };
-    if constexpr (kPeel) {
-      for (int kt = 0; kt + 1 < nk; ++kt) stage_body(kt, std::false_type{});
-      stage_body(nk - 1, std::true_type{});
-    } else {
-      for (int kt = 0; kt < nk; ++kt) stage_body(kt, std::false_type{});
-    }
+    for (int kt = 0; kt + 1 < nk; ++kt) stage_body(kt, std::false_type{});
+    stage_body(nk - 1, std::true_type{});
     lds_barrier();  // every wave is done with the ring (all its loads were waited for) before the epilogue reuses it
     if constexpr (SAVE_U) epilogue_save_u<C>(acc, smem, g, tc);
     else epilogue<C>(acc, smem, g, tc);

@@ -8,7 +8,8 @@
 // went.
 //
 // Four launches (one workgroup for the first three when the dispatch is small, see
-// permute_small_kernel), none of which needs a count on the host:
+// permute_small_kernel; colscan and scatter in one launch when the table is at most
+// 2^16 entries, see scan_scatter_kernel), none of which needs a count on the host:
 //   1. hist     one block per chunk of 256 slots: LDS histogram -> table[e][chunk]
 //   2. colscan  one block per expert: exclusive scan of that expert's row of
 //               the table over chunks (in place) and its total -> counts[e]
@@ -35,8 +36,10 @@ constexpr int kHistThreads = kPermuteChunk;  // one slot per thread
 constexpr int kScanThreads = 256;
 constexpr int kGatherThreads = 256;
 
+// chunk_major: table[c * E + e] (the two-launch path) instead of table[e * nchunks + c].
 __global__ __launch_bounds__(kHistThreads) void hist_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
-                                                            int32_t* __restrict__ table, int64_t nchunks) {
+                                                            int32_t* __restrict__ table, int64_t nchunks,
+                                                            bool chunk_major) {
   __shared__ int h[MOE_MAX_EXPERTS];
   const int64_t c = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += kHistThreads) h[e] = 0;
@@ -47,7 +50,8 @@ __global__ __launch_bounds__(kHistThreads) void hist_kernel(const int32_t* __res
     if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);  // LDS integer atomics: order-free
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kHistThreads) table[(int64_t)e * nchunks + c] = h[e];
+  for (int e = threadIdx.x; e < E; e += kHistThreads)
+    table[chunk_major ? c * E + e : (int64_t)e * nchunks + c] = h[e];
 }
 
 // Exclusive scan of one expert's per-chunk counts, in place; total -> counts[e].
@@ -167,6 +171,143 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
       }
     }
     __syncthreads();  // the cursor updates of this step are visible to the next
+  }
+}
+
+// The column scan and the scatter in one launch, for chunk-major tables of at most kFusedTable
+// entries whose expert count is a power of two from 4 to 1024 (so E divides the 1024 entries a
+// block reads per step, and every thread keeps the same four experts): block c (one chunk) reads
+// the whole table in 16-byte loads (at most 256 KB, from L2), eight in flight per thread, and
+// sums for every expert its entries before chunk c and its total; the totals become offsets and
+// the block walks its chunk as scatter_kernel does. This costs less than a launch boundary and a
+// second pass over the table. Block 0 also stores counts and offsets. Same order, same results
+// as the three-launch path.
+constexpr int kFusedThreads = 256;
+constexpr int64_t kFusedTable = int64_t(1) << 16;
+
+__global__ __launch_bounds__(kFusedThreads) void scan_scatter_kernel(const int32_t* __restrict__ ids, int64_t S,
+                                                                     int E, int id_bits,
+                                                                     const int32_t* __restrict__ table,
+                                                                     int64_t nchunks, int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ perm,
+                                                                     int32_t* __restrict__ inv) {
+  __shared__ int off_s[MOE_MAX_EXPERTS + 1];
+  __shared__ int cursor[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c = blockIdx.x;
+  constexpr int kSteps = kPermuteChunk / 64;
+  // this chunk's ids, loaded before the table so that both are in flight together
+  int id_reg[kSteps];
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int64_t s = c * kPermuteChunk + step * 64 + lane;
+    id_reg[step] = (wave == 0 && s < S) ? ids[s] : -1;
+  }
+  for (int e = tid; e < E; e += kFusedThreads) {
+    off_s[e] = 0;
+    cursor[e] = 0;
+  }
+  __syncthreads();
+  // Thread tid reads 16-byte groups tid, tid + 256, ...: entries 4 tid + 1024 i, always experts
+  // e0..e0+3 with e0 = 4 tid mod E, of chunk rows (4 tid + 1024 i) / E.
+  const int4* t4 = reinterpret_cast<const int4*>(table);
+  const int64_t n4 = nchunks * E / 4;
+  const int e0 = (4 * tid) % E;
+  int before[4] = {0, 0, 0, 0}, total[4] = {0, 0, 0, 0};
+  constexpr int kBatch = 8;
+  for (int64_t f0 = tid; f0 < n4; f0 += (int64_t)kFusedThreads * kBatch) {
+    int4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t f = f0 + (int64_t)kFusedThreads * u;
+      v[u] = f < n4 ? t4[f] : int4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t f = f0 + (int64_t)kFusedThreads * u;
+      const bool early = (4 * f) / E < c;  // entries of a chunk before this one
+      total[0] += v[u].x; total[1] += v[u].y; total[2] += v[u].z; total[3] += v[u].w;
+      if (early) {
+        before[0] += v[u].x; before[1] += v[u].y; before[2] += v[u].z; before[3] += v[u].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // LDS integer atomics: order-free
+    if (total[q] != 0) atomicAdd(&off_s[e0 + q], total[q]);
+    if (before[q] != 0) atomicAdd(&cursor[e0 + q], before[q]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // offsets = exclusive scan of the totals: each lane sums a run of 16 experts, then a wave-wide scan
+    constexpr int kPer = (MOE_MAX_EXPERTS + 63) / 64;
+    int run[kPer];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane * kPer + i;
+      run[i] = (e < E) ? off_s[e] : 0;
+      local += run[i];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += up;
+    }
+    int acc = incl - local;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane * kPer + i;
+      if (e < E) {
+        if (c == 0) counts[e] = run[i];
+        off_s[e] = acc;
+      }
+      acc += run[i];
+    }
+    if (lane == 63) off_s[E] = incl;
+  }
+  __syncthreads();
+  if (c == 0) {
+    for (int e = tid; e <= E; e += kFusedThreads) offsets[e] = off_s[e];
+  }
+  for (int e = tid; e < E; e += kFusedThreads) cursor[e] += off_s[e];
+  __syncthreads();
+  if (wave != 0) return;  // one wave walks the chunk (no barrier below this point)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int64_t s = c * kPermuteChunk + step * 64 + lane;
+    const int e = id_reg[step];
+    const bool keep = (s < S) && ((unsigned)e < (unsigned)E);
+    uint64_t same = __ballot(keep);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int leader = keep ? (__ffsll((long long)same) - 1) : lane;
+    int base = 0;
+    if (keep && lane == leader) {
+      base = cursor[e];
+      cursor[e] = base + __popcll(same);
+    }
+    base = __shfl(base, leader, 64);
+    if (s < S) {
+      if (keep) {
+        const int pos = base + rank;  // < offsets[e+1] <= S when ids are unchanged since the histogram
+        if ((int64_t)pos < S) perm[pos] = (int32_t)s;
+        inv[s] = pos;
+      } else {
+        inv[s] = -1;
+      }
+    }
+    // this step's cursor updates land before the next step's leaders read them (one wave: an LDS wait
+    // and a compiler fence take the place of the workgroup barrier)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -346,9 +487,15 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int3
   if (nchunks <= kSmallChunks && (int64_t)E * nchunks <= kSmallTable) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, ids, S, E, bits_for(E),
                        (int)nchunks, counts, offsets, perm, inv);
+  } else if ((int64_t)E * nchunks <= kFusedTable && E >= 4 && (E & (E - 1)) == 0 &&
+             (reinterpret_cast<uintptr_t>(table) & 15) == 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nchunks), dim3(kHistThreads), 0, stream, ids, S, E, table,
+                       nchunks, true);
+    hipLaunchKernelGGL(scan_scatter_kernel, dim3((unsigned)nchunks), dim3(kFusedThreads), 0, stream, ids, S, E,
+                       bits_for(E), table, nchunks, counts, offsets, perm, inv);
   } else {
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nchunks), dim3(kHistThreads), 0, stream, ids, S, E, table,
-                       nchunks);
+                       nchunks, false);
     hipLaunchKernelGGL(colscan_kernel, dim3(E), dim3(kScanThreads), 0, stream, table, nchunks, counts);
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nchunks), dim3(64), 0, stream, ids, S, E, bits_for(E), counts,
                        table, nchunks, offsets, perm, inv);

@@ -133,6 +133,10 @@ def _fuzz_cases():
         dict(T=8192, k=2, E=16, d=64, h=64, seed=17, drop_frac=0.1),
         dict(T=8193, k=2, E=16, d=64, h=64, seed=18, drop_frac=0.1),
         dict(T=2048, k=4, E=1024, d=64, h=64, seed=19, drop_frac=0.05),
+        # the two-launch permute (histogram, then scan and scatter in one launch) at its table limit of
+        # 2^16 entries (64 experts x 1024 chunks) and one chunk past it (three launches)
+        dict(T=32768, k=8, E=64, d=64, h=64, seed=20, drop_frac=0.05, empty_experts=(9,)),
+        dict(T=32800, k=8, E=64, d=64, h=64, seed=21, drop_frac=0.05),
     ]
     return cases
 
