@@ -106,7 +106,7 @@ struct ProblemList {
   int seg_lo[MOE_MAX_EXPERTS];
   int seg_rows[MOE_MAX_EXPERTS];
   int mt_prefix[MOE_MAX_EXPERTS + 1];
-  int scan_tmp[THREADS];
+  int scan_tmp[THREADS / 64];  // one total per wave
 };
 
 struct TileCoord {
@@ -232,22 +232,33 @@ __device__ void build_problem_list(const GemmArgs& g, ProblemList<THREADS>& pl) 
     mt_local[i] = mt;
     sum += mt;
   }
-  pl.scan_tmp[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < THREADS; off <<= 1) {
-    const int add = tid >= off ? pl.scan_tmp[tid - off] : 0;
-    __syncthreads();
-    pl.scan_tmp[tid] += add;
-    __syncthreads();
+  // Exclusive prefix of the per-thread sums: an inclusive scan inside each wave (shuffles), the
+  // waves' totals through LDS, then each thread adds the totals of the waves before it.
+  constexpr int kWaves = THREADS / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += up;
   }
-  int run = pl.scan_tmp[tid] - sum;
+  if (lane == 63) pl.scan_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = pl.scan_tmp[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  int run = before + incl - sum;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = tid * kPer + i;
     if (e < g.E) pl.mt_prefix[e] = run;
     run += mt_local[i];
   }
-  if (tid == THREADS - 1) pl.mt_prefix[g.E] = pl.scan_tmp[THREADS - 1];
+  if (tid == 0) pl.mt_prefix[g.E] = total;
   __syncthreads();
 }
 
