@@ -26,8 +26,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __builtin_bit_cast(float, b16 << 16);
 }
 
+// Two fp32 values to a pair of bf16 (lo in the low half), round to nearest even: one packed
+// convert (v_cvt_pk_bf16_f32) instead of two single converts, a shift and an or.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ------------------------------------------------------------------ host side

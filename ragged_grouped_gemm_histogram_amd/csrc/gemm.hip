@@ -378,20 +378,32 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
     }
   }
   lds_barrier();
+  // Thread tid takes chunk tid % OUT_CPR of rows tid / OUT_CPR + RSTEP * it: all its LDS reads
+  // first, then the stores (one read's latency instead of one per store). The stores go through a
+  // buffer resource that ends at the tile's last valid row, and a column past N gets an offset
+  // past the end: the hardware drops those stores, so no branch separates them.
   constexpr int kStoreIters = BM * C::OUT_CPR / C::THREADS;
+  constexpr int RSTEP = C::THREADS / C::OUT_CPR;
+  static_assert(C::THREADS % C::OUT_CPR == 0, "a thread keeps one chunk column");
+  const int c = tid % C::OUT_CPR, r0 = tid / C::OUT_CPR;
+  u32x4 v[kStoreIters];
 #pragma unroll
   for (int it = 0; it < kStoreIters; ++it) {
-    const int idx = it * C::THREADS + tid;
-    const int r = idx / C::OUT_CPR, c = idx % C::OUT_CPR;
-    const int64_t col = tc.n0 + c * 8;
-    if (r < tc.rows_valid && col < g.N) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16));
-      // Plain outputs (the down projection's y_perm, 256-column tiles) go out as non-temporal
-      // stores: this launch never reads them back, and allocating them in L2 would evict operand
-      // lines (-2% on the down projection in the zipf64 step, -8% back to back).
-      if constexpr (C::GATED) *reinterpret_cast<u32x4*>(g.out + (tc.row0 + r) * g.ldo + col) = v;
-      else __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(g.out + (tc.row0 + r) * g.ldo + col));
-    }
+    const int r = r0 + RSTEP * it;
+    v[it] = *reinterpret_cast<const u32x4*>(ot + r * OUT_ROW_BYTES + ((c ^ (r & (C::OUT_CPR - 1))) * 16));
+  }
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      g.out + tc.row0 * g.ldo, (short)0, (int)((int64_t)tc.rows_valid * g.ldo * 2), 0x00020000);
+  const int64_t col = tc.n0 + c * 8;
+  const uint32_t col_off = col < g.N ? (uint32_t)(col * 2) : 0x80000000u;
+  const uint32_t row_bytes = (uint32_t)(g.ldo * 2);
+#pragma unroll
+  for (int it = 0; it < kStoreIters; ++it) {
+    const uint32_t off = (uint32_t)(r0 + RSTEP * it) * row_bytes + col_off;
+    // Plain outputs (the down projection's y_perm, 256-column tiles) go out as non-temporal
+    // stores: this launch never reads them back, and allocating them in L2 would evict operand
+    // lines (-2% on the down projection in the zipf64 step, -8% back to back).
+    __builtin_amdgcn_raw_buffer_store_b128(v[it], rsrc, off, 0, C::GATED ? 0 : 2 /* nt */);
   }
   lds_barrier();  // LDS is reused by the next tile
 }
