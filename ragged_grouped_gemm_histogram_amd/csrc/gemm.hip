@@ -144,6 +144,13 @@ __device__ __forceinline__ void dma16_off(uint64_t base, uint32_t off, uint32_t 
                : "memory", "m0");
 }
 
+// A 64-bit value every lane holds the same value of, moved to SGPRs.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // A pointer every lane holds the same value of, moved to SGPRs.
 __device__ __forceinline__ uint64_t uniform_addr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -281,12 +288,14 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t t, int64_t n_tiles, int 
     const int mid = (lo_e + hi_e) >> 1;
     if (pl.mt_prefix[mid] <= gm) lo_e = mid; else hi_e = mid;
   }
+  // every lane holds the same coordinates (LDS reads of the problem list): keep them in scalar
+  // registers, where the epilogue's buffer descriptor and the load bases need them
   TileCoord c;
-  c.e = lo_e;
-  c.mi = gm - pl.mt_prefix[lo_e];
-  c.row0 = (int64_t)pl.seg_lo[lo_e] + (int64_t)c.mi * BM;
-  c.rows_valid = min(BM, pl.seg_rows[lo_e] - c.mi * BM);
-  c.n0 = nt * TILE_N;
+  c.e = __builtin_amdgcn_readfirstlane(lo_e);
+  c.mi = __builtin_amdgcn_readfirstlane(gm - pl.mt_prefix[lo_e]);
+  c.row0 = uniform_i64((int64_t)pl.seg_lo[lo_e] + (int64_t)c.mi * BM);
+  c.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, pl.seg_rows[lo_e] - c.mi * BM));
+  c.n0 = uniform_i64(nt * TILE_N);
   return c;
 }
 
@@ -346,12 +355,14 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::FM][C::FN], unsi
       for (int j = 0; j < half_fn; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          // g and u rounded to bf16 two at a time (one packed convert per pair)
           float hv[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][4 * q + s]));
-            const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + half_fn][4 * q + s]));
-            hv[s] = swiglu(gv, uv);
+          for (int s = 0; s < 4; s += 2) {
+            const uint32_t g2 = pack_bf16x2(acc[i][j][4 * q + s], acc[i][j][4 * q + s + 1]);
+            const uint32_t u2 = pack_bf16x2(acc[i][j + half_fn][4 * q + s], acc[i][j + half_fn][4 * q + s + 1]);
+            hv[s] = swiglu(bf16_bits_to_f32(g2 & 0xFFFFu), bf16_bits_to_f32(u2 & 0xFFFFu));
+            hv[s + 1] = swiglu(bf16_bits_to_f32(g2 >> 16), bf16_bits_to_f32(u2 >> 16));
           }
           const int col = wn * (BN / 2 / C::WGN) + j * 32 + 8 * q + 4 * half_lane;
           const int c = col >> 3;
@@ -440,29 +451,44 @@ __device__ __forceinline__ void epilogue_save_u(const f32x16 (&acc)[C::FM][C::FN
     }
   }
   lds_barrier();
+  // As the plain epilogue: thread tid takes gate chunk tid % HALF of rows tid / HALF + RSTEP * it,
+  // all its LDS reads first, then U and H stores through buffer resources that end at the tile's
+  // last valid row (columns past N get an offset past the end).
   const int64_t ldu = 2 * g.N;
   constexpr int kIters = BM * HALF / C::THREADS;
+  constexpr int RSTEP = C::THREADS / HALF;
+  static_assert(C::THREADS % HALF == 0, "a thread keeps one chunk column");
+  const int c = tid % HALF, r0 = tid / HALF;
+  u32x4 gv[kIters], uv[kIters];
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
-    const int idx = it * C::THREADS + tid;
-    const int r = idx / HALF, c = idx % HALF;
-    const int64_t col = tc.n0 + c * 8;
-    if (r < tc.rows_valid && col < g.N) {
-      const u32x4 gu = *reinterpret_cast<const u32x4*>(ut + r * U_ROW_BYTES + ((c ^ (r & (U_CPR - 1))) * 16));
-      const u32x4 uu =
-          *reinterpret_cast<const u32x4*>(ut + r * U_ROW_BYTES + (((c + HALF) ^ (r & (U_CPR - 1))) * 16));
-      uint16_t* urow = g.u_out + (tc.row0 + r) * ldu;
-      *reinterpret_cast<u32x4*>(urow + col) = gu;
-      *reinterpret_cast<u32x4*>(urow + g.N + col) = uu;
-      u32x4 hv;
+    const int r = r0 + RSTEP * it;
+    gv[it] = *reinterpret_cast<const u32x4*>(ut + r * U_ROW_BYTES + ((c ^ (r & (U_CPR - 1))) * 16));
+    uv[it] = *reinterpret_cast<const u32x4*>(ut + r * U_ROW_BYTES + (((c + HALF) ^ (r & (U_CPR - 1))) * 16));
+  }
+  const __amdgpu_buffer_rsrc_t u_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      g.u_out + tc.row0 * ldu, (short)0, (int)((int64_t)tc.rows_valid * ldu * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t h_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      g.out + tc.row0 * g.ldo, (short)0, (int)((int64_t)tc.rows_valid * g.ldo * 2), 0x00020000);
+  const int64_t col = tc.n0 + c * 8;
+  const bool col_ok = col < g.N;
+  const uint32_t u_col = col_ok ? (uint32_t)(col * 2) : 0x80000000u;
+  const uint32_t h_col = col_ok ? (uint32_t)(col * 2) : 0x80000000u;
+  const uint32_t up_bytes = (uint32_t)(g.N * 2);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float h0 = swiglu(bf16_bits_to_f32(gu[w] & 0xFFFFu), bf16_bits_to_f32(uu[w] & 0xFFFFu));
-        const float h1 = swiglu(bf16_bits_to_f32(gu[w] >> 16), bf16_bits_to_f32(uu[w] >> 16));
-        hv[w] = pack_bf16x2(h0, h1);
-      }
-      *reinterpret_cast<u32x4*>(g.out + (tc.row0 + r) * g.ldo + col) = hv;
+  for (int it = 0; it < kIters; ++it) {
+    const uint32_t r = (uint32_t)(r0 + RSTEP * it);
+    const uint32_t u_off = r * (uint32_t)(ldu * 2) + u_col;
+    __builtin_amdgcn_raw_buffer_store_b128(gv[it], u_rsrc, u_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(uv[it], u_rsrc, col_ok ? u_off + up_bytes : u_off, 0, 0);
+    u32x4 hv;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float h0 = swiglu(bf16_bits_to_f32(gv[it][w] & 0xFFFFu), bf16_bits_to_f32(uv[it][w] & 0xFFFFu));
+      const float h1 = swiglu(bf16_bits_to_f32(gv[it][w] >> 16), bf16_bits_to_f32(uv[it][w] >> 16));
+      hv[w] = pack_bf16x2(h0, h1);
     }
+    __builtin_amdgcn_raw_buffer_store_b128(hv, h_rsrc, r * (uint32_t)(g.ldo * 2) + h_col, 0, 0);
   }
   lds_barrier();  // LDS is reused by the next tile
 }
