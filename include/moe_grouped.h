@@ -178,8 +178,8 @@ moe_status moe_gemm_up_swiglu_u(const uint16_t* x_perm, const int32_t* offsets, 
                                 uint16_t* u_buf, hipStream_t stream);
 
 /* The first half with the permuted gather fused into its loads (OLMo report
- * Sec 9.4: the up/gate projection reads the dispatch buffer directly instead
- * of a permuted copy). Sorted row p of expert e's block reads token row
+ * Sec 9.4: GEMM 1 takes its A rows straight from the dispatch order, with no
+ * permuted copy in between). Sorted row p of expert e's block reads token row
  * x[perm[p] / k]; nothing else changes:
  *
  *   x        bf16  [T, d]    token rows
