@@ -510,6 +510,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int wm_u = __builtin_amdgcn_readfirstlane(wm);  // the same, as a scalar: branches on it stay uniform
 
   build_problem_list<C::BM>(g, pl);
   const int total_mt = pl.mt_prefix[g.E];
@@ -677,6 +678,38 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
     // (zipf64) and 4% (square). The launch that also keeps U has no registers to spare for it
     // (the compiler spills).
     const bool late_issue = !SAVE_U && NST == 2 && C::NWAVES == 8 && wave >= 4;
+    // A wave whose rows all lie past the expert's block (the last row tile of an expert) does no
+    // matrix work: it keeps its share of every stage's loads and the barrier sequence of the waves
+    // that compute (the same issues, waits and barriers as below), without fragment reads or MFMAs.
+    // Its accumulators stay zero and feed no stored row.
+    if (wm_u * C::WTM >= tc.rows_valid) {
+      if constexpr (NST == 2) {
+        issue(0);
+        if (nk > 1) {
+          issue(1);
+          wait_vmcnt_lds<OPS, true>();
+        } else {
+          wait_vmcnt_lds<0, true>();
+        }
+        bare_barrier();
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+          if (late_issue && kt > 0) issue(kt + 1);
+          wait_vmcnt_lds<0, true>();
+          bare_barrier();
+          if (!late_issue && kt + 2 < nk) issue(kt + 2);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+          if (s < nk) issue(s);
+        for (int kt = 0; kt < nk; ++kt) {
+          wait_stage(kt);
+#pragma unroll
+          for (int ks = 0; ks < BK / 16; ++ks)
+            if (kt + NST - 1 < nk) issue_part(kt + NST - 1, ks, BK / 16);
+        }
+      }
+    } else {
     // Both slots of a 2-slot ring are free at the tile start: fill them and wait for the first
     // only, so the second has a whole stage more to land (0.5-1.5% faster, bit-identical).
     if constexpr (NST == 2) {
@@ -734,6 +767,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
     };
     for (int kt = 0; kt + 1 < nk; ++kt) stage_body(kt, std::false_type{});
     stage_body(nk - 1, std::true_type{});
+    }
     lds_barrier();  // every wave is done with the ring (all its loads were waited for) before the epilogue reuses it
     if constexpr (SAVE_U) epilogue_save_u<C>(acc, smem, g, tc);
     else epilogue<C>(acc, smem, g, tc);
