@@ -155,6 +155,24 @@ class StepRun:
         if ev is not None:
             ev[4].record()
 
+    def stage_calls(self) -> dict:
+        """Each stage of the step on its own, reading the buffers an earlier step left (idempotent)."""
+        moe, wl = self.moe, self.wl
+
+        def permute():
+            moe.moe_permute(self.x, self.ids, wl.E, x_perm=self.x_perm, counts=self.counts, offsets=self.offsets,
+                            perm=self.perm, inv_map=self.inv, workspace=self.ws, gather=not self.fused)
+
+        def gemm_up():
+            if self.fused:
+                moe.moe_gemm_up_swiglu_gather(self.x, self.perm, self.offsets, self.w_ug, wl.k, h_buf=self.h_buf)
+            else:
+                moe.moe_gemm_up_swiglu(self.x_perm, self.offsets, self.w_ug, h_buf=self.h_buf)
+
+        return {"permute": permute, "gemm_up_swiglu": gemm_up,
+                "gemm_down": lambda: moe.moe_gemm_down(self.h_buf, self.offsets, self.w_down, y_perm=self.y_perm),
+                "unpermute": lambda: moe.moe_unpermute(self.y_perm, self.inv, self.rw, y=self.y)}
+
 
 STAGES = ["permute", "gemm_up_swiglu", "gemm_down", "unpermute"]
 
@@ -204,6 +222,39 @@ def time_step(torch, step, steps: int, warmup: int, graph: bool = True) -> dict:
             "stage_ms": stage_ms, "step_events": step_events}
 
 
+def time_stages_graph(torch, calls: dict, reps: int = 10, rounds: int = 5) -> dict | None:
+    """Each stage alone, `reps` back-to-back launches captured in one HIP graph, replayed `rounds` times between
+    HIP events: the per-launch time without host launch gaps (the eager stage times include them, which for the
+    ~10 us permute is a third of its time). Median over the rounds, ms per launch."""
+    out = {}
+    try:
+        for name, fn in calls.items():
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for _ in range(reps):
+                        fn()
+            torch.cuda.current_stream().wait_stream(side)
+            g.replay()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(rounds):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / reps)
+            out[name] = sorted(times)[len(times) // 2]
+            del g
+    except Exception:  # capture unavailable: the eager stage times stand alone
+        torch.cuda.synchronize()
+        return None
+    return out
+
+
 def stage_table(stage_ms: dict, algo: dict, M: int, d: int, h: int) -> dict:
     """Per-stage mean time with its rate: GB/s of algorithmic bytes for the HBM-bound permutations, TFLOP/s for
     the GEMMs (plus their algorithmic-byte rate, the bound of weight-streaming shapes)."""
@@ -231,6 +282,7 @@ def measure_config(torch, moe, name: str, dev, steps: int, warmup: int, fused: b
     wl = make_workload(name)
     run = StepRun(torch, moe, wl, dev, fused)
     tm = time_step(torch, run.step, steps, warmup)
+    sg = time_stages_graph(torch, run.stage_calls()) if tm["graph_ms"] is not None else None
     cnt = run.counts.cpu().tolist()
     M = sum(cnt)
     nonempty = sum(c > 0 for c in cnt)
@@ -245,6 +297,7 @@ def measure_config(torch, moe, name: str, dev, steps: int, warmup: int, fused: b
            "eager_ms_per_step": tm["eager_ms"], "useful_TFLOP/s": flops / (ms * 1e-3) / 1e12,
            "pct_of_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "step_events": tm["step_events"], "stages": stage_table(tm["stage_ms"], algo, M, wl.d, wl.h),
+           "stages_graph_ms": sg,
            "histogram": histogram_stats(cnt, t1), "down_tile_rows": t2}
     del run
     torch.cuda.empty_cache()
@@ -473,6 +526,7 @@ def main(argv=None):
     x_perm, y_perm, counts, offsets, inv, ws = run.x_perm, run.y_perm, run.counts, run.offsets, run.inv, run.ws
     tm = time_step(torch, run.step, args.steps, args.warmup, graph=not args.eager)
     eager_ms, graph_ms, graph_note, replay = tm["eager_ms"], tm["graph_ms"], tm["graph_note"], tm["replay"]
+    stages_graph = time_stages_graph(torch, run.stage_calls()) if graph_ms is not None else None
     stage_ms, step_events = tm["stage_ms"], tm["step_events"]
 
     M = int(offsets[-1].item())
@@ -560,6 +614,8 @@ def main(argv=None):
         "step_events": step_events,
         "useful_gflop": flops / 1e9,
         "stages": stages,
+        # each stage alone in graph replays (no host launch gaps), ms per launch
+        "stages_graph_ms": stages_graph,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "histogram": hist,
