@@ -20,7 +20,7 @@ import oracle
 import ragged_grouped_gemm_histogram_amd as moe
 from gpu_util import DeviceInputs, bits, oracle_result, say, to_dev, to_dev_bf16, workload
 from parity import assert_fails, compare_bf16, compare_swiglu_of_u
-from workloads import WORKLOADS, make_random
+from workloads import WORKLOADS, make_counts, make_random
 
 pytestmark = pytest.mark.gpu
 
@@ -159,6 +159,36 @@ def test_random_cases(case):
     # the fused-gather path runs the same arithmetic on the same rows: identical bits
     y2, p2, h2, yp2 = run_path(wl, fused=True)
     assert torch.equal(y2, y) and torch.equal(h2[:M], h_buf[:M]) and torch.equal(yp2[:M], y_perm[:M])
+
+
+# Exact expert sizes whose last row tile ends on and next to every wave-row boundary: in the last tile of an
+# expert, waves whose rows all lie past the block skip their matrix work (they keep only their loads and
+# barriers). The 256-row tiles have wave rows of 64 (gate/up, waves 4x2) and 128 (down, waves 2x4), the
+# 128-row tiles of 64; remainders of 1, 64, 65, 128, 129, 192, 193, 255 and 256 rows cover every count of
+# skipping waves in both, and the shapes are large enough that each side takes the tile height named.
+COUNT_CASES = [
+    # 256-row tiles on both sides (>= 384 rows per expert, enough 256-row tiles to occupy the device)
+    dict(T=8192, k=2, E=9, d=1024, h=1024, seed=31, w_sigma=0.03,
+         counts=[6 * 256 + r for r in (1, 64, 65, 128, 129, 192, 193, 255, 256)]),
+    # 128-row tiles (too few 256-row tiles to occupy the device)
+    dict(T=2048, k=2, E=9, d=1024, h=1024, seed=32, w_sigma=0.03,
+         counts=[2 * 128 + r for r in (1, 32, 63, 64, 65, 96, 127, 128, 0)]),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", COUNT_CASES, ids=["tiles256", "tiles128"])
+def test_expert_tails_at_wave_row_boundaries(case):
+    wl = make_counts(**case)
+    say(f"[gpu] exact-count case {case}")
+    di = DeviceInputs(wl)
+    y, p, h_buf, y_perm = run_path(wl, di=di)
+    ref = oracle.moe_expert_forward(wl.x, wl.expert_ids, wl.routing_w, wl.w_ug, wl.w_down, keep_u=True)
+    np.testing.assert_array_equal(ref.counts, np.asarray(case["counts"]))
+    check_all(wl, ref, y, p, h_buf, y_perm, di)
+    M = ref.M
+    chained = oracle.grouped_projection(bits(h_buf)[:M], ref.offsets, wl.w_down)
+    say("  y_perm from the GPU's h_buf " + str(compare_bf16(bits(y_perm)[:M], chained, "y_perm (chained)")))
 
 
 def test_negative_controls_fail_the_comparison():

@@ -61,3 +61,21 @@ def test_projection_inputs_cpu():
     a2, w2 = projection_inputs(64, 48, 40, 3, seed=5)
     assert torch.equal(a.view(torch.int16), a2.view(torch.int16)) and torch.equal(w.view(torch.int16), w2.view(torch.int16))
     assert 0.8 < float(a.float().std()) < 1.2 and 0.015 < float(w.float().std()) < 0.025
+
+
+def test_exact_count_workload():
+    from workloads import make_counts
+
+    counts = [3, 0, 5, 1]
+    wl = make_counts(T=5, k=2, E=4, d=8, h=8, counts=counts, seed=7)
+    ids = wl.expert_ids.reshape(-1)
+    assert ids.shape == (10,)
+    np.testing.assert_array_equal(np.bincount(ids[ids >= 0], minlength=4), counts)
+    assert int((ids < 0).sum()) == 10 - sum(counts)
+    assert wl.routing_w.shape == (5, 2) and np.allclose(wl.routing_w.sum(axis=1), 1.0, atol=1e-6)
+    try:
+        make_counts(T=2, k=2, E=2, d=8, h=8, counts=[3, 2], seed=1)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("more rows than slots must be refused")

@@ -214,6 +214,22 @@ def make_random(T: int, k: int, E: int, d: int, h: int, seed: int, drop_frac: fl
     return _finish(rng, name, T, k, E, d, h, ids, w, x_sigma, w_sigma, f"random T={T} k={k} E={E} d={d} h={h}")
 
 
+def make_counts(T: int, k: int, E: int, d: int, h: int, counts, seed: int, w_sigma: float = 0.05,
+                name: str = "counts") -> Workload:
+    """Exact rows per expert: expert e gets counts[e] of the T*k slots (placed in random slots, duplicates
+    within a token allowed), every other slot an invalid id (-1)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    if counts.shape != (E,) or counts.min(initial=0) < 0 or counts.sum() > T * k:
+        raise ValueError("counts must be E non-negative numbers summing to at most T*k")
+    rng = np.random.default_rng(seed)
+    flat = np.full(T * k, -1, dtype=np.int32)
+    flat[: counts.sum()] = np.repeat(np.arange(E, dtype=np.int32), counts)
+    ids = rng.permutation(flat).reshape(T, k)
+    w = _softmax_rows(rng.standard_normal((T, k), dtype=np.float32)) if T * k else np.zeros((T, k), np.float32)
+    return _finish(rng, name, T, k, E, d, h, ids, w, 1.0, w_sigma,
+                   f"exact counts T={T} k={k} E={E} d={d} h={h} rows {counts.tolist()}")
+
+
 # --------------------------------------------------------------------------
 # Inputs of the single-projection sweeps (OLMo report, Sec 9.6, Figs 38-40)
 # --------------------------------------------------------------------------
