@@ -710,63 +710,63 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_pipe_kernel(GemmArgs 
         }
       }
     } else {
-    // Both slots of a 2-slot ring are free at the tile start: fill them and wait for the first
-    // only, so the second has a whole stage more to land (0.5-1.5% faster, bit-identical).
-    if constexpr (NST == 2) {
-      issue(0);
-      if (nk > 1) {
-        issue(1);
-        wait_vmcnt_lds<OPS, true>();
-        bare_barrier();
+      // Both slots of a 2-slot ring are free at the tile start: fill them and wait for the first
+      // only, so the second has a whole stage more to land (0.5-1.5% faster, bit-identical).
+      if constexpr (NST == 2) {
+        issue(0);
+        if (nk > 1) {
+          issue(1);
+          wait_vmcnt_lds<OPS, true>();
+          bare_barrier();
+        } else {
+          wait_stage(0);
+        }
       } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+          if (s < nk) issue(s);
         wait_stage(0);
       }
-    } else {
+      load_frags(0, 0, 0);
+      // One stage of the main loop; `last_c` marks the peeled last stage (no hand-off). Every
+      // other stage hands off unconditionally, so no branch merges a path with pending fragment
+      // reads into one without them (the compiler's wait bookkeeping stays exact).
+      auto stage_body = [&](int kt, auto last_c) {
+        constexpr bool kLast = decltype(last_c)::value;
+        // The slot stage kt+NST-1 fills held stage kt-1, which every wave finished
+        // reading before the barrier that made stage kt visible.
+        // With a 3-slot ring (128-row tiles) the next stage's loads are spread over the four
+        // slices; the 2-slot ring issues them a stage ahead (right after that barrier, inside the
+        // previous stage's last slice; the second wave of each SIMD one slice later, see
+        // late_issue; stage 1 at the tile start).
+        constexpr int kParts = NST >= 3 ? BK / 16 : 1;
+        const bool more = kt + NST - 1 < nk;
+        const int slot = kt % NST;
 #pragma unroll
-      for (int s = 0; s < NST - 1; ++s)
-        if (s < nk) issue(s);
-      wait_stage(0);
-    }
-    load_frags(0, 0, 0);
-    // One stage of the main loop; `last_c` marks the peeled last stage (no hand-off). Every
-    // other stage hands off unconditionally, so no branch merges a path with pending fragment
-    // reads into one without them (the compiler's wait bookkeeping stays exact).
-    auto stage_body = [&](int kt, auto last_c) {
-      constexpr bool kLast = decltype(last_c)::value;
-      // The slot stage kt+NST-1 fills held stage kt-1, which every wave finished
-      // reading before the barrier that made stage kt visible.
-      // With a 3-slot ring (128-row tiles) the next stage's loads are spread over the four
-      // slices; the 2-slot ring issues them a stage ahead (right after that barrier, inside the
-      // previous stage's last slice; the second wave of each SIMD one slice later, see
-      // late_issue; stage 1 at the tile start).
-      constexpr int kParts = NST >= 3 ? BK / 16 : 1;
-      const bool more = kt + NST - 1 < nk;
-      const int slot = kt % NST;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int cur = ks & 1;
-        if (more && ks < kParts && (NST > 2 || (late_issue && kt > 0))) issue_part(kt + NST - 1, ks, kParts);
-        if (ks + 1 < BK / 16) {
-          load_frags(cur ^ 1, slot, ks + 1);
-          mfmas(cur);
-          interleave_reads<C::FM * C::FN, C::FM + (B_NMAJOR ? 2 : 1) * C::FN>();
-        } else {
-          // The last slice's fragments are already in registers: hand the stage
-          // off first (wait, barrier, refill of the slot just drained, reads of
-          // the next stage's first slice) so that its MFMAs cover the barrier
-          // and the read latency. The MFMAs stay outside the branch so the
-          // accumulators keep one register assignment.
-          if constexpr (!kLast) {
-            wait_stage(kt + 1);
-            if (NST == 2 && kt + 2 < nk && !late_issue) issue(kt + 2);
-            load_frags(cur ^ 1, (kt + 1) % NST, 0);
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int cur = ks & 1;
+          if (more && ks < kParts && (NST > 2 || (late_issue && kt > 0))) issue_part(kt + NST - 1, ks, kParts);
+          if (ks + 1 < BK / 16) {
+            load_frags(cur ^ 1, slot, ks + 1);
+            mfmas(cur);
+            interleave_reads<C::FM * C::FN, C::FM + (B_NMAJOR ? 2 : 1) * C::FN>();
+          } else {
+            // The last slice's fragments are already in registers: hand the stage
+            // off first (wait, barrier, refill of the slot just drained, reads of
+            // the next stage's first slice) so that its MFMAs cover the barrier
+            // and the read latency. The MFMAs stay outside the branch so the
+            // accumulators keep one register assignment.
+            if constexpr (!kLast) {
+              wait_stage(kt + 1);
+              if (NST == 2 && kt + 2 < nk && !late_issue) issue(kt + 2);
+              load_frags(cur ^ 1, (kt + 1) % NST, 0);
+            }
+            mfmas(cur);
           }
-          mfmas(cur);
         }
-      }
-    };
-    for (int kt = 0; kt + 1 < nk; ++kt) stage_body(kt, std::false_type{});
-    stage_body(nk - 1, std::true_type{});
+      };
+      for (int kt = 0; kt + 1 < nk; ++kt) stage_body(kt, std::false_type{});
+      stage_body(nk - 1, std::true_type{});
     }
     lds_barrier();  // every wave is done with the ring (all its loads were waited for) before the epilogue reuses it
     if constexpr (SAVE_U) epilogue_save_u<C>(acc, smem, g, tc);
