@@ -66,6 +66,7 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_NULL_POINTER = 1,       /* a pointer is NULL while its tensor is non-empty           */
   MOE_ERR_BAD_SHAPE = 2,          /* T<0, k<1, E<1 or E>1024, d or h < 8 or not a multiple of 8,
+                                     d or h > 2^24 (> 2^20 for the grouped GEMM calls),
                                      T*k >= 2^31, or cap_rows < 0                               */
   MOE_ERR_MISALIGNED = 3,         /* a bf16 tensor not 16-byte aligned, or an int32/float
                                      tensor not 4-byte aligned                                  */

@@ -37,9 +37,15 @@ inline bool bad_width(int64_t w) { return w < 8 || (w % 8) != 0 || w > (int64_t(
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// The GEMM epilogues store a tile of up to 256 output rows through one buffer resource with 32-bit
+// byte offsets (and an offset of 2^31 for columns past the end). The widest output row is U's 2h
+// columns, so 256 * 2 * 2^20 * 2 bytes = 2^30 keeps every offset of a tile below 2^31.
+constexpr int64_t kMaxGemmWidth = int64_t(1) << 20;
+
 moe_status check_gemm_shape(int64_t cap_rows, int64_t d, int64_t h, int32_t E) {
   if (cap_rows < 0 || cap_rows > kMaxSlots || bad_width(d) || bad_width(h) || E < 1 || E > MOE_MAX_EXPERTS)
     return MOE_ERR_BAD_SHAPE;
+  if (d > kMaxGemmWidth || h > kMaxGemmWidth) return MOE_ERR_BAD_SHAPE;
   return MOE_OK;
 }
 

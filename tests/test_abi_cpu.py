@@ -119,6 +119,21 @@ def test_gemm_validation(lib, fn, kw, status):
     assert gemm(lib, fn, **kw) == status
 
 
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid sizes with placeholder pointers: host without a GPU only")
+def test_gemm_width_limit(lib):
+    # a 256-row output tile is addressed with 32-bit offsets: d and h stop at 2^20 for every grouped GEMM call
+    top = 1 << 20
+    for fn in ("moe_gemm_up_swiglu", "moe_gemm_down"):
+        assert gemm(lib, fn, d=top, h=top) == DEV
+        assert gemm(lib, fn, d=top + 8) == SHAPE and gemm(lib, fn, h=top + 8) == SHAPE
+    assert lib.moe_gemm_up_swiglu_u(FAKE, FAKE, FAKE, 16, 16, top + 8, 2, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_gemm_up_swiglu_gather(FAKE, FAKE, 8, 2, FAKE, FAKE, top + 8, 16, 2, FAKE, None) == SHAPE
+    assert dgrad(lib, d_in=top + 8) == SHAPE and wgrad(lib, d_out=top + 8) == SHAPE
+    # the permute and unpermute rows stay valid up to 2^24 columns
+    assert permute(lib, d=top + 8) == DEV
+    assert lib.moe_unpermute(FAKE, FAKE, FAKE, 4, 2, top + 8, FAKE, None) == DEV
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(d=12), SHAPE), (dict(E=0), SHAPE), (dict(T=2**30, k=2), SHAPE),
     (dict(x=None), NULLP), (dict(perm=None), NULLP), (dict(offs=None), NULLP), (dict(w=None), NULLP),
