@@ -102,10 +102,12 @@ def histogram_stats(counts, tile_rows: int) -> dict:
             "grouped_tile_rows": tile_rows, "grouped_tile_padding": (1 - M / slots) if slots else 0.0}
 
 
-def gemm_tile_rows(M_cap: int, E: int, N_tiles: int, cus: int = 256) -> int:
-    """Row-tile height the grouped GEMM launch picks (256 when the mean block has >= 384 rows and its 256-row
-    tiles can occupy every CU, else 128); the rule the library applies on the host."""
-    return 256 if (M_cap >= 384 * E and (M_cap // 256 + E) * N_tiles >= cus) else 128
+def gemm_tile_rows(M_cap: int, E: int, N_tiles: int, cus: int = 256, down: bool = False) -> int:
+    """Row-tile height the grouped GEMM launch picks (256 when the mean block has >= 384 rows, or for the down
+    projection 192 to 256 rows, and its 256-row tiles can occupy every CU, else 128); the rule the library
+    applies on the host."""
+    tall = M_cap >= 384 * E or (down and 192 * E <= M_cap <= 256 * E)
+    return 256 if (tall and (M_cap // 256 + E) * N_tiles >= cus) else 128
 
 
 class StepRun:
@@ -291,7 +293,7 @@ def measure_config(torch, moe, name: str, dev, steps: int, warmup: int, fused: b
     algo = algorithmic_bytes(wl.T, wl.k, M, wl.d, wl.h, nonempty, fused)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     t1 = gemm_tile_rows(wl.T * wl.k, wl.E, -(-wl.h // 128), cus)
-    t2 = gemm_tile_rows(wl.T * wl.k, wl.E, -(-wl.d // 256), cus)
+    t2 = gemm_tile_rows(wl.T * wl.k, wl.E, -(-wl.d // 256), cus, down=True)
     out = {"workload": name, "seed": WORKLOADS[name][0], "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "h": wl.h,
            "M": M, "ms_per_step": ms, "timing": "graph replays" if tm["graph_ms"] is not None else "eager",
            "eager_ms_per_step": tm["eager_ms"], "useful_TFLOP/s": flops / (ms * 1e-3) / 1e12,

@@ -1298,10 +1298,22 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
   if (g.K % BK == 0 && offsets_fit_32(g)) {
     // 256-row tiles need large expert blocks, and enough of them to occupy every CU: at most
     // cap_rows/256 + E row tiles exist whatever the offsets; when even that many cannot fill the
-    // device, 128-row tiles (twice the tiles, a deeper ring) finish sooner.
+    // device, 128-row tiles (twice the tiles, a deeper ring) finish sooner. The host knows only
+    // the mean rows per expert (cap_rows / E). From 384 on, 256-row tiles are faster. Below it an
+    // expert's last tile decides: a 256-row tile costs about 1.6 of a 128-row one (its loads set
+    // the stage time), so an expert of 129-256 rows is cheaper as one 256-row tile than as two
+    // 128-row tiles, and one of 257-384 rows as three 128-row tiles than as two 256-row ones.
+    // The down projection (N-contiguous weights) follows that count for a mean of 192-256 rows:
+    // balanced 16-expert d = h = 4096 projections at 192 and 256 rows per expert 10-15% faster,
+    // the same at 128 and 320, the Qwen3-shaped down projection 1-4% faster. The gate/up
+    // projection keeps 128-row tiles below 384 (on the Qwen3-shaped workload 256-row tiles made
+    // it 11% slower: an expert's tail then costs a whole 2048-deep tile).
     const int64_t tile_n = GATED ? BigTile<GATED>::OUTW : BigTile<GATED>::BN;
     const int64_t big_tiles = (g.cap_rows / BigTile<GATED>::BM + g.E) * ((g.N + tile_n - 1) / tile_n);
-    if (g.cap_rows >= (int64_t)384 * g.E && big_tiles >= device_cu_count(current_device())) {
+    const int64_t rows = g.cap_rows;
+    const bool tall = rows >= (int64_t)384 * g.E ||
+                      (!GATED && B_NMAJOR && rows >= (int64_t)192 * g.E && rows <= (int64_t)256 * g.E);
+    if (tall && big_tiles >= device_cu_count(current_device())) {
       static std::atomic<bool> done[64] = {};
       using Big = BigTile<GATED, SAVE_U>;
       return launch_kernel<Big>(grouped_gemm_pipe_kernel<Big, B_NMAJOR, SAVE_U>, done, g, stream);

@@ -99,5 +99,10 @@ def test_tile_height_rule():
     # zipf64: 65,536 slots over 64 experts, 6 gate/up column tiles -> 256-row tiles; Qwen3-shaped: 128
     assert bench.gemm_tile_rows(65536, 64, 6) == 256
     assert bench.gemm_tile_rows(32768, 128, 6) == 128
+    # the down projection takes 256-row tiles for a mean of 192-256 rows per expert as well
+    assert bench.gemm_tile_rows(32768, 128, 8, down=True) == 256
+    assert bench.gemm_tile_rows(24576, 128, 8, down=True) == 256
+    assert bench.gemm_tile_rows(40960, 128, 8, down=True) == 128
+    assert bench.gemm_tile_rows(2048, 16, 16, down=True) == 128
     # the edge workload: blocks are large, but its 256-row tiles could not occupy 256 CUs
     assert bench.gemm_tile_rows(4096, 8, 3) == 128

@@ -135,6 +135,39 @@ def test_capacity_sweep_ends(M):
     say("  " + str(_check_sampled(a, w, y, offs, per_expert=2, seed=2)))
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M", [3072, 4096])
+def test_down_tall_tiles_balanced(M):
+    """The down projection takes 256-row tiles for a mean of 192-256 rows per expert: balanced
+    16-expert d = h = 4096 projections at 192 and 256 rows per expert (Fig 38's operands)."""
+    E, dim = 16, 4096
+    say(f"[gpu] down projection, tall tiles, balanced M={M}")
+    a, w = projection_inputs(M, dim, dim, E, seed=38, device="cuda:0")
+    offs = _offsets(balanced_counts(E, M))
+    y = moe.moe_gemm_down(a, to_dev(offs), w)
+    torch.cuda.synchronize()
+    say("  " + str(_check_sampled(a, w, y, offs, per_expert=4, seed=3)))
+
+
+def test_down_tall_tiles_ragged():
+    """Ragged experts averaging 224 rows (256-row tiles for the down projection): each expert's last tile
+    holds 1 to 255 rows, so the waves skipping their matrix work vary from tile to tile; compared whole."""
+    rng = np.random.default_rng(224)
+    E, K, N = 32, 256, 2048
+    counts = rng.integers(150, 299, size=E)
+    counts[3], counts[17] = 0, 1
+    counts[5] += 224 * E - int(counts.sum())
+    assert 192 * E <= counts.sum() <= 256 * E and counts.min() >= 0
+    M = int(counts.sum())
+    say(f"[gpu] down projection, tall tiles, ragged counts={counts.tolist()}")
+    a = to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w = to_bf16_bits(0.05 * rng.standard_normal((E, K, N), dtype=np.float32))
+    offs = _offsets(counts)
+    y = moe.moe_gemm_down(to_dev_bf16(a), to_dev(offs), to_dev_bf16(w))
+    torch.cuda.synchronize()
+    say("  " + str(compare_bf16(bits(y), oracle.grouped_projection(a, offs, w), "y")))
+
+
 @pytest.mark.parametrize("T,K,N", [(300, 1024, 4096), (128, 8192, 81920)], ids=["small", "fig39-T128"])
 def test_decomposition_eq17(T, K, N):
     """Eq 17 on the GPU: 4 or 8 column-block experts over the repeated input give the dense
