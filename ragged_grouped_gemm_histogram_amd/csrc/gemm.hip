@@ -1304,7 +1304,7 @@ hipError_t launch_grouped(const GemmArgs& g, hipStream_t stream) {
     // the stage time), so an expert of 129-256 rows is cheaper as one 256-row tile than as two
     // 128-row tiles, and one of 257-384 rows as three 128-row tiles than as two 256-row ones.
     // The down projection (N-contiguous weights) follows that count for a mean of 192-256 rows:
-    // balanced 16-expert d = h = 4096 projections at 192 and 256 rows per expert 10-15% faster,
+    // balanced 16-expert d = h = 4096 projections at 192 and 256 rows per expert 11-16% faster,
     // the same at 128 and 320, the Qwen3-shaped down projection 1-4% faster. The gate/up
     // projection keeps 128-row tiles below 384 (on the Qwen3-shaped workload 256-row tiles made
     // it 11% slower: an expert's tail then costs a whole 2048-deep tile).
