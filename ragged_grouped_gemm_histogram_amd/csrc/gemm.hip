@@ -206,16 +206,6 @@ __device__ __forceinline__ int logical_worker() {
   return (b % 8) * (G / 8) + b / 8;
 }
 
-// A row feeding sorted row p: p itself, or (fused gather) the token of dispatch
-// slot a_rows[p], clamped into the token range.
-__device__ __forceinline__ int64_t a_row_of(const GemmArgs& g, int64_t p) {
-  if (g.a_rows == nullptr) return p;
-  int64_t slot = g.a_rows[p];
-  const int64_t cap = g.a_tokens * g.a_k;
-  slot = slot < 0 ? 0 : (slot >= cap ? cap - 1 : slot);
-  return slot / g.a_k;
-}
-
 // Problem list from the device offsets, clamped so no access leaves the buffers:
 // per expert its first row, its row count and the prefix of its m-tile counts.
 template <int BM, int THREADS>
@@ -826,16 +816,35 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_regs_kernel(GemmArgs 
 
     u32x4 ra[C::A_LOADS];
     u32x4 rb[C::B_LOADS];
+    // Start of each of this thread's A rows (or -1 past the expert's block), fetched once per tile:
+    // with the fused gather all the rows' dispatch slots are in flight together.
+    int64_t a_row_start[C::A_LOADS];
+    {
+      int32_t slot[C::A_LOADS];
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i) {
+        const int r = (i * C::THREADS + tid) / kChunksK;
+        slot[i] = (g.a_rows != nullptr && r < tc.rows_valid) ? g.a_rows[tc.row0 + r] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i) {
+        const int r = (i * C::THREADS + tid) / kChunksK;
+        int64_t row = tc.row0 + r;
+        if (g.a_rows != nullptr) {
+          const int64_t cap = g.a_tokens * g.a_k;
+          const int64_t sl = slot[i] < 0 ? 0 : (slot[i] >= cap ? cap - 1 : slot[i]);
+          row = sl / g.a_k;
+        }
+        a_row_start[i] = r < tc.rows_valid ? row * g.lda : -1;
+      }
+    }
     auto load_a = [&](int kt) {
       const int64_t k0 = (int64_t)kt * BK;
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
-        const int idx = i * C::THREADS + tid;
-        const int r = idx / kChunksK, c = idx % kChunksK;
+        const int c = (i * C::THREADS + tid) % kChunksK;
         const int64_t kk = k0 + c * 8;
-        ra[i] = (r < tc.rows_valid && kk < g.K)
-                    ? *reinterpret_cast<const u32x4*>(g.A + a_row_of(g, tc.row0 + r) * g.lda + kk)
-                    : zero4();
+        ra[i] = (a_row_start[i] >= 0 && kk < g.K) ? *reinterpret_cast<const u32x4*>(g.A + a_row_start[i] + kk) : zero4();
       }
     };
     auto load_b = [&](int kt) {
