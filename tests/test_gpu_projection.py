@@ -55,8 +55,9 @@ def _check_sampled(a, w, y, offsets, per_expert=2, seed=0, what="y"):
     ([0, 37, 300, 1, 129, 0, 513], 320, 576),   # ragged, empty experts, 128-row tiles
     ([700, 900, 420, 0, 1100], 192, 8712),       # large blocks, enough tiles to fill the device: 256-row tiles
     ([5, 0, 260, 77], 328, 200),                 # K and N not multiples of 64: zero-staged K remainder
+    ([700, 900, 420, 0, 1100], 200, 8712),       # a K remainder on the 256-row tiles
     ([1], 64, 64),                               # one row
-], ids=["ragged", "big-tiles", "k-tail", "one-row"])
+], ids=["ragged", "big-tiles", "k-tail", "big-k-tail", "one-row"])
 def test_projection_whole(counts, K, N):
     say(f"[gpu] projection counts={counts} K={K} N={N}")
     rng = np.random.default_rng(sum(counts) + K)

@@ -28,8 +28,9 @@ def _offsets(counts):
     ([700, 900, 420], 128, 4480),                 # large blocks, enough tiles to fill the device: 256-row tiles
     ([0, 37, 300, 1, 129, 0, 513], 320, 288),     # 128-row tiles, empty experts, partial last column tile
     ([5, 0, 260, 77], 328, 200),                  # K not a multiple of 64: zero-staged K remainder
+    ([700, 900, 420], 200, 4480),                 # a K remainder on the 256-row tiles
     ([1], 64, 64),                                # one row
-], ids=["big-tiles", "ragged", "k-tail", "one-row"])
+], ids=["big-tiles", "ragged", "k-tail", "big-k-tail", "one-row"])
 def test_save_u_forward(counts, d, h):
     say(f"[gpu] save-U forward counts={counts} d={d} h={h}")
     rng = np.random.default_rng(sum(counts) + d + h)
